@@ -1,0 +1,168 @@
+/*
+ * pkv.h - grouped-query attention over a paged KV cache on AMD MI355X (gfx950).
+ *
+ * C ABI of libpkv.so.  Every tensor argument is a plain DEVICE pointer owned by
+ * the caller; the library allocates no memory, keeps no state between calls
+ * (apart from a cached device-property query), never synchronises, and only
+ * enqueues work on the HIP stream passed in `stream` (a hipStream_t; NULL is
+ * the default stream).  bf16 tensors are raw bfloat16 bit patterns, densely
+ * packed (row-major, innermost dimension contiguous), 16-byte aligned.
+ *
+ * Cache format (flex paged-attention commit page, "Why this works", points
+ * 1 and 3): one pool per K and per V of shape
+ *     [num_kv_heads][num_pages * page_size][head_dim]   (bf16)
+ * and a page table [num_slots][max_blocks] (int32) mapping (batch slot,
+ * logical block) to a physical page.  Batch slot 0 and page 0 are reserved
+ * padding: a row in slot 0 has no valid key.
+ *
+ * Error behaviour: every entry point returns PKV_OK (0) once its kernels are
+ * enqueued, or a negative PKV_E* code, with a message in pkv_last_error().
+ * All argument checks are host-side and happen before any HIP call.  Values
+ * that live in device memory (page ids, slots, lengths, positions) are not
+ * checked by the host; the kernels clamp them so that no access leaves the
+ * buffers described by the size arguments, and results for out-of-contract
+ * values are unspecified.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_OK 0
+#define PKV_E_NULL (-1)      /* a required pointer is NULL */
+#define PKV_E_SHAPE (-2)     /* a size argument is out of range or inconsistent */
+#define PKV_E_ALIGN (-3)     /* a bf16 tensor pointer is not 16-byte aligned */
+#define PKV_E_WORKSPACE (-4) /* workspace missing or smaller than required */
+#define PKV_E_SPLITS (-5)    /* num_splits out of range */
+#define PKV_E_HIP (-6)       /* a HIP launch failed; message has hipGetErrorString */
+
+/* paged_decode_attn flags */
+#define PKV_F_ASSUME_CONTIGUOUS (1u << 0) /* caller promises each row's pages are consecutive ids */
+#define PKV_F_NO_CONTIG_DETECT (1u << 1)  /* always walk the page table block by block */
+
+#define PKV_MAX_SPLITS 64
+
+/*
+ * paged_kv_append - write new tokens' K and V into their pages.
+ *
+ * Defined by the cache update that runs before attention in the attention
+ * forward of the qwen3_flex_inference.py page (update(input_pos, k, v,
+ * batch_idx)).  Token t (0 <= t < num_tokens) with slot s = batch_idx[t] and
+ * logical position p = input_pos[t] is written, for every KV head h, to pool
+ * row  page_table[s][p / page_size] * page_size + p % page_size.  The copy is
+ * bit-exact.  A token is skipped (nothing written) when s == 0, when its
+ * block maps to page 0, or when s, p / page_size or the page lies outside
+ * [1, num_slots), [0, max_blocks), [1, num_pages).  Two tokens naming the same
+ * (slot, position) in one call is undefined.
+ *
+ *   k_pool, v_pool   bf16 [num_kv_heads][num_pages*page_size][head_dim], written
+ *   page_table       int32 [num_slots][max_blocks]
+ *   batch_idx        int32 [num_tokens]
+ *   input_pos        int32 [num_tokens]
+ *   k_new, v_new     bf16 [num_tokens][num_kv_heads][head_dim]
+ *
+ * num_tokens == 0 is a valid no-op.  head_dim must be 64 or 128, page_size a
+ * power of two >= 16.
+ */
+int paged_kv_append(void *k_pool, void *v_pool, int32_t num_pages, int32_t page_size,
+                    int32_t num_kv_heads, int32_t head_dim, const int32_t *page_table,
+                    int32_t num_slots, int32_t max_blocks, const int32_t *batch_idx,
+                    const int32_t *input_pos, int32_t num_tokens, const void *k_new,
+                    const void *v_new, void *stream);
+
+/*
+ * paged_decode_workspace_size - bytes of workspace paged_decode_attn needs
+ * for `num_splits` key splits (0 for num_splits <= 1).  Pure host function.
+ */
+size_t paged_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                                   int32_t num_splits);
+
+/*
+ * paged_decode_num_splits - the split count paged_decode_attn chooses when
+ * called with num_splits = 0 on the current device.  Host function.
+ */
+int32_t paged_decode_num_splits(int32_t batch, int32_t num_kv_heads, int32_t max_kv_len);
+
+/*
+ * paged_decode_attn - one query token per row attends to its row's cached keys.
+ *
+ * Defined by the decode attention of the qwen3_flex_inference.py page: the
+ * block mask's causal offset lets row r see logical keys 0..input_pos, so the
+ * row has kv_len[r] = input_pos + 1 valid keys (the token just appended
+ * included), reached through the page table; flex_attention runs with
+ * scale and enable_gqa.  Query head h reads KV head h / (num_q_heads /
+ * num_kv_heads).  For row r with slot s = batch_idx[r] and n = kv_len[r]:
+ *     x_j   = scale * q[r][h] . K[s, j]           j < n
+ *     O     = sum_j softmax(x)_j V[s, j]          (fp32 accumulation, bf16 result)
+ *     LSE   = ln sum_j exp(x_j)                   (fp32)
+ * A row with s == 0 or n == 0 (a padding row, flex_vs_vllm.md page, "What
+ * broke correctness") returns O = +0.0 and LSE = -inf, never NaN.  Pool
+ * bytes outside the row's valid keys never influence the result.
+ *
+ *   q            bf16 [batch][num_q_heads][head_dim]
+ *   k_pool,v_pool bf16 [num_kv_heads][num_pages*page_size][head_dim]
+ *   page_table   int32 [num_slots][max_blocks]
+ *   batch_idx    int32 [batch]
+ *   kv_len       int32 [batch]; values above max_blocks*page_size are clamped
+ *   max_kv_len   host upper bound of kv_len used to plan key splits (<= 0 or
+ *                above max_blocks*page_size means max_blocks*page_size); a
+ *                loose bound costs speed, never correctness
+ *   num_splits   0 = choose automatically, 1 = single pass, 2..PKV_MAX_SPLITS
+ *                = split-K partials plus a log-sum-exp merge kernel
+ *   flags        PKV_F_* above
+ *   workspace    device buffer of paged_decode_workspace_size(...) bytes for the
+ *                chosen split count (may be NULL when that size is 0)
+ *   out          bf16 [batch][num_q_heads][head_dim]
+ *   lse          fp32 [batch][num_q_heads]
+ *
+ * Results are bitwise reproducible for identical inputs and split count.
+ * batch == 0 is a valid no-op.  Requirements: head_dim 64 or 128,
+ * num_q_heads a multiple of num_kv_heads with at most 16 query heads per
+ * KV head, page_size a power of two >= 16.
+ */
+int paged_decode_attn(const void *q, const void *k_pool, const void *v_pool, int32_t num_pages,
+                      int32_t page_size, int32_t num_kv_heads, int32_t head_dim,
+                      const int32_t *page_table, int32_t num_slots, int32_t max_blocks,
+                      const int32_t *batch_idx, const int32_t *kv_len, int32_t batch,
+                      int32_t num_q_heads, float scale, int32_t max_kv_len, int32_t num_splits,
+                      uint32_t flags, void *workspace, size_t workspace_bytes, void *out,
+                      float *lse, void *stream);
+
+/*
+ * packed_prefill_attn - document-causal attention over packed prompts.
+ *
+ * Defined by the prefill of the qwen3_flex_inference.py page: prompts are
+ * concatenated into one sequence and masked so that each token sees only
+ * tokens of its own document up to itself; GQA and scale as in decode.
+ * Documents are the row ranges [cu_seqlens[d], cu_seqlens[d+1]); row i of
+ * document d attends to keys j in [cu_seqlens[d], i].  K and V are read from
+ * the packed arrays (write them into pages separately with paged_kv_append).
+ *
+ *   q            bf16 [total_len][num_q_heads][head_dim]
+ *   k, v         bf16 [total_len][num_kv_heads][head_dim]
+ *   cu_seqlens   int32 [num_docs+1], device; cu[0] = 0, non-decreasing,
+ *                cu[num_docs] = total_len (zero-length documents allowed)
+ *   out          bf16 [total_len][num_q_heads][head_dim]
+ *   lse          fp32 [total_len][num_q_heads] (natural log)
+ *
+ * total_len == 0 is a valid no-op.  Requirements: head_dim 128, num_q_heads a
+ * multiple of num_kv_heads.
+ */
+int packed_prefill_attn(const void *q, const void *k, const void *v, const int32_t *cu_seqlens,
+                        int32_t num_docs, int32_t total_len, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim, float scale, void *out,
+                        float *lse, void *stream);
+
+/* Text for the most recent non-zero status returned on this thread. */
+const char *pkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,27 @@
+"""GQA attention over a paged KV cache for AMD MI355X (gfx950).
+
+Three operations, each a hand-written HIP kernel path behind the C ABI of
+libpkv.so (include/pkv.h):
+
+  paged_kv_append      scatter new tokens' K/V into their pages
+  paged_decode_attn    one query token per row over its paged keys
+                       (single pass or split-K + log-sum-exp merge,
+                       contiguous-page fast path)
+  packed_prefill_attn  document-causal attention over packed prompts
+
+This package is the thin Python binding: it marshals torch tensors into the
+C calls and nothing else.
+"""
+from ._binding import (  # noqa: F401
+    LIB_PATH,
+    PKV_F_ASSUME_CONTIGUOUS,
+    PKV_F_NO_CONTIG_DETECT,
+    PKV_MAX_SPLITS,
+    last_error,
+    load_library,
+    packed_prefill_attn,
+    paged_decode_attn,
+    paged_decode_num_splits,
+    paged_decode_workspace_size,
+    paged_kv_append,
+)

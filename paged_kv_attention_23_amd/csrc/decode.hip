@@ -1,0 +1,467 @@
+// Paged decode attention (one query token per row) and the split-K merge.
+//
+// What is computed is the decode attention of the qwen3_flex_inference.py
+// page: row r attends to logical keys 0..kv_len-1 of its slot, routed through
+// the page table, with GQA (H_q / H_kv query heads per KV head) and scale.
+// How it is computed is MI355X-specific:
+//
+//  * One workgroup of 4 waves owns a (row, KV head, split) unit and reads each
+//    K/V row of its key range exactly once, serving all G query heads of that
+//    KV head.  Waves interleave over 32-key tiles of the range.
+//  * Scores: S^T[key][head] = K Q^T on the 16x16x32 bf16 matrix core, K
+//    loaded straight from HBM into the A-operand layout (lane = key row,
+//    16 contiguous bytes), Q held in B-operand registers for the whole unit
+//    (heads past G are zero columns).
+//  * Online softmax in base 2 in fp32 registers: each lane owns one head and
+//    eight keys of the tile; the tile max needs two cross-row shuffles.
+//  * O^T[d][head] += V^T P^T on the matrix core.  The score layout already is
+//    the B operand P^T (key order permuted consistently); V^T is read from a
+//    per-wave LDS tile whose 4-key chunks are padded so the transposed reads
+//    hit distinct banks.
+//  * The contiguous fast path (flex_vs_vllm.md page, option table: blocks
+//    are contiguous) replaces per-block page-table lookups with one linear
+//    row base when a unit's pages are consecutive ids.
+//  * Split-K (flash-decoding) writes normalised fp32 partials and their
+//    log-sum-exp; a separate kernel merges them.
+#include <math.h>
+
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+constexpr int kDecWaves = 4;
+constexpr int kDecThreads = kDecWaves * kWave;
+constexpr int kTileKeys = 32;
+
+template <int D>
+struct DecGeom {
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kChunkBytes = 4 * kRowBytes + 32;  // 4 key rows, then 32 B of padding
+  static constexpr int kVBytes = (kTileKeys / 4) * kChunkBytes;  // one wave's V tile
+  static constexpr int kDChunks = D / 32;    // QK steps over head_dim
+  static constexpr int kDBlocks = D / 16;    // PV output blocks over head_dim
+  static constexpr int kVLoads = D / 16;     // 16-byte V loads per lane per tile
+  static constexpr int kLanesPerRow = D / 8; // lanes covering one key row in a V load
+  static constexpr int kKeysPerLoad = kWave / kLanesPerRow;
+  static constexpr int kMergeFloats = kDecWaves * 16 * D + kDecWaves * 16 * 2;
+  static constexpr int kSmemBytes = (kDecWaves * kVBytes > kMergeFloats * 4) ? kDecWaves * kVBytes
+                                                                               : kMergeFloats * 4;
+};
+
+// Where the keys of one (row, KV head) unit live.  Page ids of 64
+// consecutive logical blocks starting at wbase sit one per lane in pwin, so
+// a lookup is a single v_readlane with a wave-uniform index.
+struct RowCtx {
+  const int32_t *pt_row;  // page-table row of the slot
+  int64_t contig_base;    // pool row of logical key 0 when contig
+  int page_shift, num_pages, max_blocks, hi;
+  int wbase;              // first logical block held in pwin
+  int pwin;               // per lane: page id of block wbase + lane
+  bool contig;
+};
+
+__device__ __forceinline__ void load_window(RowCtx &c, int wbase, int lane) {
+  c.wbase = wbase;
+  const int b = wbase + lane;
+  c.pwin = (b < c.max_blocks) ? c.pt_row[b] : 0;
+}
+
+// Pool row of the first key of a 16-key block (key0 is a multiple of 16 and
+// page_size >= 16, so the block sits in one page).  Blocks wholly past the
+// valid keys point at row 0, which always exists; their values are masked.
+__device__ __forceinline__ int64_t block_row(const RowCtx &c, int key0) {
+  if (key0 >= c.hi) return 0;
+  if (c.contig) return c.contig_base + key0;
+  int page = __builtin_amdgcn_readlane(c.pwin, (key0 >> c.page_shift) - c.wbase);
+  page = min(max(page, 0), c.num_pages - 1);
+  return ((int64_t)page << c.page_shift) + (key0 & ((1 << c.page_shift) - 1));
+}
+
+// Make sure both blocks of the tile starting at kt are inside the window.
+__device__ __forceinline__ void ensure_window(RowCtx &c, int kt, int lane) {
+  if (c.contig) return;
+  const int last = min(kt + kTileKeys, c.hi) - 1;
+  if ((last >> c.page_shift) - c.wbase >= kWave) load_window(c, kt >> c.page_shift, lane);
+}
+
+template <int D>
+__device__ __forceinline__ void load_k(u32x4 (&k)[2][D / 32], const RowCtx &c,
+                                       const uint16_t *kbase, int kt, int lane) {
+  const int hl = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const uint16_t *kr = kbase + (block_row(c, kt + 16 * b) + hl) * D + 8 * lg;
+#pragma unroll
+    for (int ch = 0; ch < D / 32; ++ch) k[b][ch] = *reinterpret_cast<const u32x4 *>(kr + 32 * ch);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void load_v(u32x4 (&v)[D / 16], const RowCtx &c, const uint16_t *vbase,
+                                       int kt, int lane) {
+  using Gm = DecGeom<D>;
+  const int64_t row0 = block_row(c, kt), row1 = block_row(c, kt + 16);
+#pragma unroll
+  for (int i = 0; i < Gm::kVLoads; ++i) {
+    const int key = i * Gm::kKeysPerLoad + lane / Gm::kLanesPerRow;  // key within the tile
+    const int64_t rb = (i * Gm::kKeysPerLoad < 16) ? row0 : row1;     // a load never straddles blocks
+    v[i] = *reinterpret_cast<const u32x4 *>(vbase + (rb + (key & 15)) * D +
+                                            (lane % Gm::kLanesPerRow) * 8);
+  }
+}
+
+// Stage a tile's V rows in this wave's LDS tile; keys past the range become
+// zeros (0 * NaN would otherwise poison the accumulation).
+template <int D>
+__device__ __forceinline__ void store_v(const u32x4 (&v)[D / 16], char *vlds, int kt, int hi,
+                                        int lane) {
+  using Gm = DecGeom<D>;
+  const bool tail = kt + kTileKeys > hi;
+#pragma unroll
+  for (int i = 0; i < Gm::kVLoads; ++i) {
+    const int key = i * Gm::kKeysPerLoad + lane / Gm::kLanesPerRow;
+    u32x4 val = v[i];
+    if (tail && kt + key >= hi) val = u32x4{0u, 0u, 0u, 0u};
+    const int off = (key >> 2) * Gm::kChunkBytes + (key & 3) * Gm::kRowBytes +
+                    (lane % Gm::kLanesPerRow) * 16;
+    *reinterpret_cast<u32x4 *>(vlds + off) = val;
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void compute_tile(const u32x4 (&k)[2][D / 32], int kt, int hi,
+                                             const char *vlds, const bf16x8 *qop, float &m_run,
+                                             float &l_run, f32x4 *o, float scale_log2, int lane) {
+  using Gm = DecGeom<D>;
+  const int hl = lane & 15, lg = lane >> 4;
+  const bool tail = kt + kTileKeys > hi;
+
+  // 1) scores for two 16-key blocks: S^T = K Q^T
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ch = 0; ch < Gm::kDChunks; ++ch) {
+    s0 = mfma16x16x32(as_bf16x8(k[0][ch]), qop[ch], s0);
+    s1 = mfma16x16x32(as_bf16x8(k[1][ch]), qop[ch], s1);
+  }
+
+  // 2) online softmax, base 2.  Lane holds keys 4*lg+i (block 0) and
+  //    16+4*lg+i (block 1) of head hl.
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = s0[i] * scale_log2;
+    x[4 + i] = s1[i] * scale_log2;
+  }
+  if (tail) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int key = kt + (i < 4 ? 4 * lg + i : 16 + 4 * lg + (i - 4));
+      if (key >= hi) x[i] = -INFINITY;
+    }
+  }
+  float mt = x[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) mt = fmaxf(mt, x[i]);
+  mt = fmaxf(mt, shfl_xor_f(mt, 16));
+  mt = fmaxf(mt, shfl_xor_f(mt, 32));
+  const float m_new = fmaxf(m_run, mt);
+  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+  const float alpha = fast_exp2(m_run - m_use);
+  float p[8];
+  float psum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    p[i] = fast_exp2(x[i] - m_use);
+    psum += p[i];
+  }
+  l_run = l_run * alpha + psum;
+  m_run = m_new;
+#pragma unroll
+  for (int t = 0; t < Gm::kDBlocks; ++t) o[t] *= alpha;
+
+  // 3) P^T is already in B-operand form: element e of k-group lg is key
+  //    kappa(lg, e) = e < 4 ? 4*lg + e : 16 + 4*lg + (e - 4).
+  const u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                    pack_bf16x2(p[6], p[7])};
+  const bf16x8 pop = as_bf16x8(pw);
+
+  // 4) O^T += V^T P^T.  PV step t uses V^T rows d(t, m) = NT*m + t
+  //    (NT = D/16 steps): lane (hl, lg) reads the NT consecutive values
+  //    V[key][NT*hl .. NT*hl+NT-1] once per key kappa(lg, e) and feeds every
+  //    step from them.  Accumulator (t, i) of lane (hl, lg) is therefore
+  //    O[head hl][NT*(4*lg+i) + t].
+  constexpr int NT = Gm::kDBlocks;
+  constexpr int NW = NT / 2;  // 32-bit words per lane per key
+  uint32_t rv[8][NW];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int key = e < 4 ? 4 * lg + e : 16 + 4 * lg + (e - 4);
+    const char *src = vlds + (key >> 2) * Gm::kChunkBytes + (key & 3) * Gm::kRowBytes + 2 * NT * hl;
+    if constexpr (NW == 4) {
+      const u32x4 w = *reinterpret_cast<const u32x4 *>(src);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) rv[e][j] = w[j];
+    } else {
+      const u32x2 w = *reinterpret_cast<const u32x2 *>(src);
+#pragma unroll
+      for (int j = 0; j < NW; ++j) rv[e][j] = w[j];
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t a0 = rv[2 * j][t >> 1], a1 = rv[2 * j + 1][t >> 1];
+      w[j] = (t & 1) ? ((a0 >> 16) | (a1 & 0xffff0000u)) : ((a0 & 0xffffu) | (a1 << 16));
+    }
+    const u32x4 vw = {w[0], w[1], w[2], w[3]};
+    o[t] = mfma16x16x32(as_bf16x8(vw), pop, o[t]);
+  }
+}
+
+// Result of a unit with no valid key: O = +0, LSE = -inf (single pass), or a
+// partial with LSE = -inf that the merge gives weight zero.
+__device__ void write_empty(const DecodeArgs &a, int r, int g, int sp) {
+  const int pairs = a.G * (a.D >> 1);
+  for (int idx = threadIdx.x; idx < pairs; idx += kDecThreads) {
+    const int h = g * a.G + idx / (a.D >> 1);
+    const int d = 2 * (idx % (a.D >> 1));
+    const int64_t rh = (int64_t)r * a.H_q + h;
+    if (a.num_splits == 1) {
+      *reinterpret_cast<uint32_t *>(a.out + rh * a.D + d) = 0u;
+      if (d == 0) a.lse[rh] = -INFINITY;
+    } else {
+      const int64_t prh = (int64_t)sp * a.B * a.H_q + rh;
+      *reinterpret_cast<f32x2 *>(a.o_part + prh * a.D + d) = f32x2{0.f, 0.f};
+      if (d == 0) a.lse_part[prh] = -INFINITY;
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_kernel(DecodeArgs a) {
+  using Gm = DecGeom<D>;
+  __shared__ __attribute__((aligned(16))) char smem[Gm::kSmemBytes];
+
+  // blockIdx.x enumerates (split, KV head, row), split fastest.
+  const int sp = blockIdx.x % a.num_splits;
+  const int g = (blockIdx.x / a.num_splits) % a.H_kv;
+  const int r = blockIdx.x / (a.num_splits * a.H_kv);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
+  const int hl = lane & 15, lg = lane >> 4;
+  const int G = a.G;
+
+  const int s = a.batch_idx[r];
+  int n = a.kv_len[r];
+  n = min(n, a.max_blocks << a.page_shift);
+  const bool pad = (s <= 0) || (s >= a.num_slots) || (n <= 0);
+  const int64_t lo64 = (int64_t)sp * a.chunk;
+  const int lo = (int)min(lo64, (int64_t)n);
+  const int hi = (sp == a.num_splits - 1) ? n : (int)min((int64_t)n, lo64 + a.chunk);
+  if (pad || lo >= hi) {
+    write_empty(a, r, g, sp);
+    return;
+  }
+
+  // Where this unit's keys live; detect consecutive page ids (one wave vote).
+  RowCtx c;
+  c.pt_row = a.page_table + (int64_t)s * a.max_blocks;
+  c.page_shift = a.page_shift;
+  c.num_pages = a.num_pages;
+  c.max_blocks = a.max_blocks;
+  c.hi = hi;
+  c.contig = false;
+  c.contig_base = 0;
+  const int blk_lo = lo >> a.page_shift;
+  load_window(c, blk_lo, lane);
+  if (a.contig_mode != 2) {
+    const int nb = ((hi - 1) >> a.page_shift) - blk_lo + 1;
+    const int first = __builtin_amdgcn_readfirstlane(c.pwin);
+    bool ok = first >= 0 && first + nb <= a.num_pages;
+    if (a.contig_mode == 0 && ok) {
+      ok = __all(lane >= nb || c.pwin == first + lane);
+      for (int b0 = kWave; b0 < nb && ok; b0 += kWave) {
+        const int b = b0 + lane;
+        ok = __all(b >= nb || c.pt_row[blk_lo + b] == first + b);
+      }
+    }
+    c.contig = ok;
+    c.contig_base = ((int64_t)first - blk_lo) << a.page_shift;
+  }
+
+  const uint16_t *kbase = a.k_pool + (int64_t)g * a.plane_rows * D;
+  const uint16_t *vbase = a.v_pool + (int64_t)g * a.plane_rows * D;
+
+  // Q^T as B operands: column hl = query head g*G + hl (zero past G).
+  bf16x8 qop[Gm::kDChunks];
+  {
+    const uint16_t *qr = a.q + ((int64_t)r * a.H_q + g * G + hl) * D + 8 * lg;
+#pragma unroll
+    for (int ch = 0; ch < Gm::kDChunks; ++ch) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (hl < G) w = *reinterpret_cast<const u32x4 *>(qr + 32 * ch);
+      qop[ch] = as_bf16x8(w);
+    }
+  }
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 o[Gm::kDBlocks];
+#pragma unroll
+  for (int t = 0; t < Gm::kDBlocks; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  char *vlds = smem + wave * Gm::kVBytes;
+  const int ntiles = (hi - lo + kTileKeys - 1) / kTileKeys;
+
+  // Software pipeline: K of the next tile goes to the other register set and
+  // V of the next tile to the staging registers while the current tile is
+  // computed; two K sets, one V set (staged to LDS first thing each step).
+  u32x4 ka[2][D / 32], kb[2][D / 32], vr[D / 16];
+  int t = wave;
+  if (t < ntiles) {
+    ensure_window(c, lo + t * kTileKeys, lane);
+    load_v<D>(vr, c, vbase, lo + t * kTileKeys, lane);
+    load_k<D>(ka, c, kbase, lo + t * kTileKeys, lane);
+  }
+  while (t < ntiles) {
+    store_v<D>(vr, vlds, lo + t * kTileKeys, hi, lane);
+    int tn = t + kDecWaves;
+    if (tn < ntiles) {
+      ensure_window(c, lo + tn * kTileKeys, lane);
+      load_v<D>(vr, c, vbase, lo + tn * kTileKeys, lane);
+      load_k<D>(kb, c, kbase, lo + tn * kTileKeys, lane);
+    }
+    compute_tile<D>(ka, lo + t * kTileKeys, hi, vlds, qop, m_run, l_run, o, a.scale_log2, lane);
+    t = tn;
+    if (t >= ntiles) break;
+    store_v<D>(vr, vlds, lo + t * kTileKeys, hi, lane);
+    tn = t + kDecWaves;
+    if (tn < ntiles) {
+      ensure_window(c, lo + tn * kTileKeys, lane);
+      load_v<D>(vr, c, vbase, lo + tn * kTileKeys, lane);
+      load_k<D>(ka, c, kbase, lo + tn * kTileKeys, lane);
+    }
+    compute_tile<D>(kb, lo + t * kTileKeys, hi, vlds, qop, m_run, l_run, o, a.scale_log2, lane);
+    t = tn;
+  }
+
+  // Combine the 4 waves through LDS (the merge area reuses the V tiles).
+  l_run += shfl_xor_f(l_run, 16);
+  l_run += shfl_xor_f(l_run, 32);
+  __syncthreads();
+  float *mo = reinterpret_cast<float *>(smem);        // [wave][16 heads][D]
+  float *mm = mo + kDecWaves * 16 * D;                // [wave][16]
+  float *ml = mm + kDecWaves * 16;                    // [wave][16]
+  if (hl < G) {
+    constexpr int NT = Gm::kDBlocks;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) mo[(wave * 16 + hl) * D + NT * (4 * lg + i) + tt] = o[tt][i];
+    if (lg == 0) {
+      mm[wave * 16 + hl] = m_run;
+      ml[wave * 16 + hl] = l_run;
+    }
+  }
+  __syncthreads();
+
+  const int pairs = G * (D / 2);
+  for (int idx = threadIdx.x; idx < pairs; idx += kDecThreads) {
+    const int hh = idx / (D / 2);
+    const int d = 2 * (idx % (D / 2));
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, mm[w * 16 + hh]);
+    float L = 0.f, o0 = 0.f, o1 = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float mw = mm[w * 16 + hh];
+      const float wt = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+      L += wt * ml[w * 16 + hh];
+      const f32x2 ov = *reinterpret_cast<const f32x2 *>(mo + (w * 16 + hh) * D + d);
+      o0 += wt * ov[0];
+      o1 += wt * ov[1];
+    }
+    const float inv = (L > 0.f) ? 1.f / L : 0.f;
+    const float lse_nat = (L > 0.f) ? (M + log2f(L)) * kLn2 : -INFINITY;
+    const int64_t rh = (int64_t)r * a.H_q + g * G + hh;
+    if (a.num_splits == 1) {
+      *reinterpret_cast<uint32_t *>(a.out + rh * D + d) = pack_bf16x2(o0 * inv, o1 * inv);
+      if (d == 0) a.lse[rh] = lse_nat;
+    } else {
+      const int64_t prh = (int64_t)sp * a.B * a.H_q + rh;
+      *reinterpret_cast<f32x2 *>(a.o_part + prh * D + d) = f32x2{o0 * inv, o1 * inv};
+      if (d == 0) a.lse_part[prh] = lse_nat;
+    }
+  }
+}
+
+// Merge of split partials: one wave per (row, query head).
+//   M = max_s L_s; LSE = M + ln sum_s exp(L_s - M); O = sum_s exp(L_s - LSE) O_s
+// Partials with L_s = -inf carry weight zero and are not read.
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t rh = (int64_t)blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
+  const int64_t nrh = (int64_t)a.B * a.H_q;
+  if (rh >= nrh) return;
+  const int S = a.num_splits;
+  const float ls = (lane < S) ? a.lse_part[(int64_t)lane * nrh + rh] : -INFINITY;
+  float M = ls;
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) M = fmaxf(M, shfl_xor_f(M, m));
+  constexpr int kPer = D / kWave;  // elements of head_dim per lane
+  if (M == -INFINITY) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) a.out[rh * D + lane * kPer + k] = 0;
+    if (lane == 0) a.lse[rh] = -INFINITY;
+    return;
+  }
+  float w = (ls == -INFINITY) ? 0.f : expf(ls - M);
+  float sum = w;
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) sum += shfl_xor_f(sum, m);
+  const float L = M + logf(sum);
+  w = (ls == -INFINITY) ? 0.f : expf(ls - L);
+  float acc[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) acc[k] = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float ws = __shfl(w, s, kWave);
+    if (ws == 0.f) continue;  // uniform: every lane sees the same ws
+    const float *op = a.o_part + ((int64_t)s * nrh + rh) * D + lane * kPer;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) acc[k] += ws * op[k];
+  }
+  if (kPer == 2) {
+    *reinterpret_cast<uint32_t *>(a.out + rh * D + lane * 2) = pack_bf16x2(acc[0], acc[kPer - 1]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+      a.out[rh * D + lane * kPer + k] = (uint16_t)(pack_bf16x2(acc[k], 0.f) & 0xffffu);
+  }
+  if (lane == 0) a.lse[rh] = L;
+}
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
+  if (a.B == 0) return hipSuccess;
+  const dim3 grid((unsigned)((int64_t)a.num_splits * a.H_kv * a.B));
+  if (a.D == 128)
+    hipLaunchKernelGGL(decode_kernel<128>, grid, dim3(kDecThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(decode_kernel<64>, grid, dim3(kDecThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.num_splits == 1) return e;
+  const int64_t nrh = (int64_t)a.B * a.H_q;
+  const unsigned mblocks = (unsigned)((nrh + 3) / 4);
+  if (a.D == 128)
+    hipLaunchKernelGGL(merge_kernel<128>, dim3(mblocks), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(merge_kernel<64>, dim3(mblocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,254 @@
+// C ABI of libpkv.so (declared in include/pkv.h): argument checks, split
+// planning and kernel dispatch.  Every check runs on the host before any HIP
+// call, so the error paths work (and are tested) without a GPU.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <atomic>
+
+#include "../../include/pkv.h"
+#include "pkv_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
+
+int log2_exact(int32_t v) {  // log2 of a power of two, else -1
+  if (v <= 0 || (v & (v - 1)) != 0) return -1;
+  int s = 0;
+  while ((1 << s) != v) ++s;
+  return s;
+}
+
+int check_pool(int32_t num_pages, int32_t page_size, int32_t num_kv_heads, int32_t head_dim,
+               int32_t num_slots, int32_t max_blocks) {
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_E_SHAPE, "head_dim must be 64 or 128 (got %d)", head_dim);
+  if (num_kv_heads <= 0) return fail(PKV_E_SHAPE, "num_kv_heads must be positive (got %d)", num_kv_heads);
+  if (log2_exact(page_size) < 4 || page_size > (1 << 20))
+    return fail(PKV_E_SHAPE, "page_size must be a power of two in [16, 2^20] (got %d)", page_size);
+  if (num_pages <= 0) return fail(PKV_E_SHAPE, "num_pages must be positive (got %d)", num_pages);
+  if ((int64_t)num_pages * page_size > INT32_MAX)
+    return fail(PKV_E_SHAPE, "num_pages*page_size exceeds 2^31-1 rows");
+  if (num_slots <= 0 || max_blocks <= 0)
+    return fail(PKV_E_SHAPE, "num_slots and max_blocks must be positive (got %d, %d)", num_slots,
+                max_blocks);
+  if ((int64_t)max_blocks * page_size > INT32_MAX)
+    return fail(PKV_E_SHAPE, "max_blocks*page_size exceeds 2^31-1 keys");
+  return PKV_OK;
+}
+
+int launch_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return PKV_OK;
+  return fail(PKV_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Compute units of the current device, cached per device id.
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+constexpr int kTileKeys = 32;
+constexpr int kMinSplitKeys = 256;
+
+int32_t auto_splits(int32_t batch, int32_t num_kv_heads, int32_t max_kv_len, int cus) {
+  const int64_t units = (int64_t)batch * num_kv_heads;
+  if (units <= 0 || max_kv_len <= 0) return 1;
+  const int64_t target = 4LL * cus;  // workgroups wanted in flight
+  int64_t s = (target + units - 1) / units;
+  const int64_t by_len = max_kv_len / kMinSplitKeys;
+  if (s > by_len) s = by_len;
+  if (s > PKV_MAX_SPLITS) s = PKV_MAX_SPLITS;
+  if (s < 1) s = 1;
+  return (int32_t)s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *pkv_last_error(void) { return g_err; }
+
+int paged_kv_append(void *k_pool, void *v_pool, int32_t num_pages, int32_t page_size,
+                    int32_t num_kv_heads, int32_t head_dim, const int32_t *page_table,
+                    int32_t num_slots, int32_t max_blocks, const int32_t *batch_idx,
+                    const int32_t *input_pos, int32_t num_tokens, const void *k_new,
+                    const void *v_new, void *stream) {
+  if (num_tokens < 0) return fail(PKV_E_SHAPE, "num_tokens must be >= 0 (got %d)", num_tokens);
+  int rc = check_pool(num_pages, page_size, num_kv_heads, head_dim, num_slots, max_blocks);
+  if (rc) return rc;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !page_table || !batch_idx || !input_pos || !k_new || !v_new)
+    return fail(PKV_E_NULL, "paged_kv_append: a required pointer is NULL");
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_new) || !aligned16(v_new))
+    return fail(PKV_E_ALIGN, "paged_kv_append: bf16 tensors must be 16-byte aligned");
+  if (!aligned4(page_table) || !aligned4(batch_idx) || !aligned4(input_pos))
+    return fail(PKV_E_ALIGN, "paged_kv_append: int32 tensors must be 4-byte aligned");
+  pkv::AppendArgs a;
+  a.k_pool = (uint16_t *)k_pool;
+  a.v_pool = (uint16_t *)v_pool;
+  a.page_table = page_table;
+  a.batch_idx = batch_idx;
+  a.input_pos = input_pos;
+  a.k_new = (const uint16_t *)k_new;
+  a.v_new = (const uint16_t *)v_new;
+  a.plane_rows = (int64_t)num_pages * page_size;
+  a.num_pages = num_pages;
+  a.page_shift = log2_exact(page_size);
+  a.num_slots = num_slots;
+  a.max_blocks = max_blocks;
+  a.num_tokens = num_tokens;
+  a.H_kv = num_kv_heads;
+  a.D = head_dim;
+  return launch_status(pkv::launch_kv_append(a, (hipStream_t)stream), "paged_kv_append launch");
+}
+
+size_t paged_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                                   int32_t num_splits) {
+  if (num_splits <= 1 || batch <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  const size_t rows = (size_t)num_splits * (size_t)batch * (size_t)num_q_heads;
+  const size_t o_bytes = (rows * (size_t)head_dim * sizeof(float) + 255) & ~(size_t)255;
+  return o_bytes + rows * sizeof(float);
+}
+
+int32_t paged_decode_num_splits(int32_t batch, int32_t num_kv_heads, int32_t max_kv_len) {
+  return auto_splits(batch, num_kv_heads, max_kv_len, device_cus());
+}
+
+int paged_decode_attn(const void *q, const void *k_pool, const void *v_pool, int32_t num_pages,
+                      int32_t page_size, int32_t num_kv_heads, int32_t head_dim,
+                      const int32_t *page_table, int32_t num_slots, int32_t max_blocks,
+                      const int32_t *batch_idx, const int32_t *kv_len, int32_t batch,
+                      int32_t num_q_heads, float scale, int32_t max_kv_len, int32_t num_splits,
+                      uint32_t flags, void *workspace, size_t workspace_bytes, void *out,
+                      float *lse, void *stream) {
+  if (batch < 0) return fail(PKV_E_SHAPE, "batch must be >= 0 (got %d)", batch);
+  int rc = check_pool(num_pages, page_size, num_kv_heads, head_dim, num_slots, max_blocks);
+  if (rc) return rc;
+  if (num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(PKV_E_SHAPE, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                num_q_heads, num_kv_heads);
+  if (num_q_heads / num_kv_heads > 16)
+    return fail(PKV_E_SHAPE, "at most 16 query heads per KV head are supported (got %d)",
+                num_q_heads / num_kv_heads);
+  if (!(scale == scale) || isinf(scale)) return fail(PKV_E_SHAPE, "scale must be finite");
+  if (num_splits < 0 || num_splits > PKV_MAX_SPLITS)
+    return fail(PKV_E_SPLITS, "num_splits must be in [0, %d] (got %d)", PKV_MAX_SPLITS, num_splits);
+  if (flags & ~(uint32_t)(PKV_F_ASSUME_CONTIGUOUS | PKV_F_NO_CONTIG_DETECT))
+    return fail(PKV_E_SHAPE, "unknown flag bits 0x%x", flags);
+  if ((int64_t)batch * num_kv_heads * PKV_MAX_SPLITS > INT32_MAX)
+    return fail(PKV_E_SHAPE, "batch*num_kv_heads too large (got %d*%d)", batch, num_kv_heads);
+  if (batch == 0) return PKV_OK;
+  if (!q || !k_pool || !v_pool || !page_table || !batch_idx || !kv_len || !out || !lse)
+    return fail(PKV_E_NULL, "paged_decode_attn: a required pointer is NULL");
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
+    return fail(PKV_E_ALIGN, "paged_decode_attn: bf16 tensors must be 16-byte aligned");
+  if (!aligned4(page_table) || !aligned4(batch_idx) || !aligned4(kv_len) || !aligned4(lse))
+    return fail(PKV_E_ALIGN, "paged_decode_attn: int32/fp32 tensors must be 4-byte aligned");
+
+  const int32_t cap = max_blocks * page_size;
+  const int32_t kv_bound = (max_kv_len <= 0 || max_kv_len > cap) ? cap : max_kv_len;
+  int32_t S = num_splits;
+  if (S == 0) S = auto_splits(batch, num_kv_heads, kv_bound, device_cus());
+  int32_t chunk = (kv_bound + S - 1) / S;
+  chunk = (chunk + kTileKeys - 1) / kTileKeys * kTileKeys;
+  if (chunk <= 0) chunk = kTileKeys;
+
+  pkv::DecodeArgs a;
+  a.o_part = nullptr;
+  a.lse_part = nullptr;
+  if (S > 1) {
+    const size_t need = paged_decode_workspace_size(batch, num_q_heads, head_dim, S);
+    if (!workspace || workspace_bytes < need)
+      return fail(PKV_E_WORKSPACE, "paged_decode_attn: %d splits need %zu workspace bytes (got %zu%s)",
+                  S, need, workspace_bytes, workspace ? "" : ", NULL");
+    if (!aligned16(workspace))
+      return fail(PKV_E_ALIGN, "paged_decode_attn: workspace must be 16-byte aligned");
+    const size_t rows = (size_t)S * batch * num_q_heads;
+    a.o_part = (float *)workspace;
+    a.lse_part = (float *)((char *)workspace + ((rows * head_dim * sizeof(float) + 255) & ~(size_t)255));
+  }
+  a.q = (const uint16_t *)q;
+  a.k_pool = (const uint16_t *)k_pool;
+  a.v_pool = (const uint16_t *)v_pool;
+  a.page_table = page_table;
+  a.batch_idx = batch_idx;
+  a.kv_len = kv_len;
+  a.plane_rows = (int64_t)num_pages * page_size;
+  a.num_pages = num_pages;
+  a.page_shift = log2_exact(page_size);
+  a.num_slots = num_slots;
+  a.max_blocks = max_blocks;
+  a.B = batch;
+  a.H_q = num_q_heads;
+  a.H_kv = num_kv_heads;
+  a.G = num_q_heads / num_kv_heads;
+  a.D = head_dim;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.num_splits = S;
+  a.chunk = chunk;
+  a.contig_mode = (flags & PKV_F_NO_CONTIG_DETECT) ? 2 : (flags & PKV_F_ASSUME_CONTIGUOUS) ? 1 : 0;
+  a.out = (uint16_t *)out;
+  a.lse = lse;
+  return launch_status(pkv::launch_decode(a, (hipStream_t)stream), "paged_decode_attn launch");
+}
+
+int packed_prefill_attn(const void *q, const void *k, const void *v, const int32_t *cu_seqlens,
+                        int32_t num_docs, int32_t total_len, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim, float scale, void *out,
+                        float *lse, void *stream) {
+  if (total_len < 0 || num_docs < 0)
+    return fail(PKV_E_SHAPE, "total_len and num_docs must be >= 0 (got %d, %d)", total_len, num_docs);
+  if (head_dim != 128) return fail(PKV_E_SHAPE, "packed_prefill_attn supports head_dim 128 (got %d)", head_dim);
+  if (num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(PKV_E_SHAPE, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                num_q_heads, num_kv_heads);
+  if (!(scale == scale) || isinf(scale)) return fail(PKV_E_SHAPE, "scale must be finite");
+  if (total_len == 0) return PKV_OK;
+  if (num_docs == 0) return fail(PKV_E_SHAPE, "total_len > 0 needs at least one document");
+  if (!q || !k || !v || !cu_seqlens || !out || !lse)
+    return fail(PKV_E_NULL, "packed_prefill_attn: a required pointer is NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(PKV_E_ALIGN, "packed_prefill_attn: bf16 tensors must be 16-byte aligned");
+  if (!aligned4(cu_seqlens) || !aligned4(lse))
+    return fail(PKV_E_ALIGN, "packed_prefill_attn: int32/fp32 tensors must be 4-byte aligned");
+  pkv::PrefillArgs a;
+  a.q = (const uint16_t *)q;
+  a.k = (const uint16_t *)k;
+  a.v = (const uint16_t *)v;
+  a.cu_seqlens = cu_seqlens;
+  a.num_docs = num_docs;
+  a.L = total_len;
+  a.H_q = num_q_heads;
+  a.H_kv = num_kv_heads;
+  a.G = num_q_heads / num_kv_heads;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.out = (uint16_t *)out;
+  a.lse = lse;
+  return launch_status(pkv::launch_prefill(a, 0, (hipStream_t)stream), "packed_prefill_attn launch");
+}
+
+}  // extern "C"

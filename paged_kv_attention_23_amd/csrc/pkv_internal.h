@@ -1,0 +1,49 @@
+// Host-side launch interfaces between the C ABI (pkv_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct AppendArgs {
+  uint16_t *k_pool, *v_pool;       // [H_kv][num_pages*page_size][D]
+  const int32_t *page_table;       // [num_slots][max_blocks]
+  const int32_t *batch_idx, *input_pos;  // [num_tokens]
+  const uint16_t *k_new, *v_new;   // [num_tokens][H_kv][D]
+  int64_t plane_rows;              // num_pages * page_size
+  int32_t num_pages, page_shift, num_slots, max_blocks;
+  int32_t num_tokens, H_kv, D;
+};
+
+struct DecodeArgs {
+  const uint16_t *q;               // [B][H_q][D]
+  const uint16_t *k_pool, *v_pool; // [H_kv][plane_rows][D]
+  const int32_t *page_table;       // [num_slots][max_blocks]
+  const int32_t *batch_idx, *kv_len;  // [B]
+  int64_t plane_rows;
+  int32_t num_pages, page_shift, num_slots, max_blocks;
+  int32_t B, H_q, H_kv, G, D;
+  float scale_log2;                // scale * log2(e)
+  int32_t num_splits, chunk;       // keys per split (multiple of the 32-key tile)
+  int32_t contig_mode;             // 0 detect per row, 1 assume contiguous, 2 never
+  float *o_part, *lse_part;        // split partials [S][B][H_q][D], [S][B][H_q]
+  uint16_t *out;                   // [B][H_q][D] bf16
+  float *lse;                      // [B][H_q]
+};
+
+struct PrefillArgs {
+  const uint16_t *q;               // [L][H_q][D]
+  const uint16_t *k, *v;           // [L][H_kv][D]
+  const int32_t *cu_seqlens;       // [num_docs+1]
+  int32_t num_docs, L, H_q, H_kv, G;
+  float scale_log2;
+  uint16_t *out;                   // [L][H_q][D]
+  float *lse;                      // [L][H_q]
+};
+
+hipError_t launch_kv_append(const AppendArgs &a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs &a, int32_t num_tiles_bound, hipStream_t stream);
+
+}  // namespace pkv

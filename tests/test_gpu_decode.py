@@ -1,0 +1,305 @@
+"""GPU parity of paged_kv_append and paged_decode_attn against the float64 oracle.
+
+Every case calls the HIP library through its C ABI (ctypes binding) and
+compares with oracle/ on the same seeded inputs.  Pools are filled with bf16
+NaN wherever no valid key lives, so any stray read shows up as NaN.
+"""
+from __future__ import annotations
+
+import functools
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import BF16_NAN, bf16_bits_to_f32, f32_to_bf16_bits, make_case, make_decode_case, \
+    make_prefill_case
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - GPU tests only run on the GPU machine
+    pytest.skip("no GPU", allow_module_level=True)
+
+import paged_kv_attention_23_amd as pkv  # noqa: E402
+from gpu_util import check_close, dev_bf16, dev_i32, host_bits  # noqa: E402
+
+
+@functools.lru_cache(maxsize=None)
+def _case(cfg):
+    return make_case(cfg, fill="nan")
+
+
+@functools.lru_cache(maxsize=None)
+def _ref(cfg):
+    """Oracle result for a decode config, after applying its append (if any)."""
+    c = _case(cfg)
+    kp, vp = c.k_pool, c.v_pool
+    if c.app_batch_idx is not None:
+        kp, vp = oracle.append_pages(kp, vp, c.num_pages, c.page_size, c.page_table,
+                                     c.app_batch_idx, c.app_input_pos, c.app_k, c.app_v)
+    out, lse = oracle.decode_case(c, kp, vp)
+    return kp, vp, out, lse
+
+
+class _Dev:
+    """Device copies of one decode case (pools after the append, if any)."""
+
+    def __init__(self, c, kp=None, vp=None):
+        self.c = c
+        self.q = dev_bf16(c.q)
+        self.k = dev_bf16(c.k_pool if kp is None else kp)
+        self.v = dev_bf16(c.v_pool if vp is None else vp)
+        self.pt = dev_i32(c.page_table)
+        self.bi = dev_i32(c.batch_idx)
+        self.kl = dev_i32(c.kv_len)
+
+    def decode(self, **kw):
+        c = self.c
+        return pkv.paged_decode_attn(self.q, self.k, self.v, self.pt, self.bi, self.kl,
+                                     page_size=c.page_size, scale=float(c.scale),
+                                     max_kv_len=int(c.kv_len.max()), **kw)
+
+
+_dev_cache = {}
+
+
+def _dev(cfg):
+    if cfg not in _dev_cache:
+        _dev_cache.clear()  # keep one large config resident at a time
+        kp, vp, _, _ = _ref(cfg)
+        _dev_cache[cfg] = _Dev(_case(cfg), kp, vp)
+    return _dev_cache[cfg]
+
+
+def _print_case(msg):
+    print(msg, flush=True)
+
+
+# ----------------------------------------------------------------------------- append
+@pytest.mark.parametrize("cfg", [1, 2, 5])
+def test_append_bit_exact(cfg):
+    """Whole-pool byte equality with the oracle's scatter (NaN-filled pools)."""
+    _print_case(f"append cfg{cfg}")
+    c = _case(cfg)
+    if cfg == 5:
+        H_kv, D, ps, P = c.H_kv, c.D, c.page_size, c.num_pages
+        kp0 = np.full((H_kv, P * ps, D), BF16_NAN, np.uint16)
+        bi, ip, kn, vn, pt = c.batch_idx, c.input_pos, c.k, c.v, c.page_table
+    elif cfg == 2:
+        kp0, ps, P = c.k_pool, c.page_size, c.num_pages
+        bi, ip, kn, vn, pt = c.app_batch_idx, c.app_input_pos, c.app_k, c.app_v, c.page_table
+    else:
+        # tiny config: append every valid key of both sequences into an empty pool
+        ps, P = c.page_size, c.num_pages
+        kp0 = np.full_like(c.k_pool, BF16_NAN)
+        rows = [(int(c.batch_idx[r]), j) for r in range(c.B) for j in range(int(c.kv_len[r]))
+                if c.batch_idx[r] != 0]
+        bi = np.array([s for s, _ in rows] + [0], np.int32)          # plus one padding token
+        ip = np.array([j for _, j in rows] + [0], np.int32)
+        phys = [int(c.page_table[s, j // ps]) * ps + j % ps for s, j in rows]
+        kn = np.concatenate([c.k_pool[:, phys, :].transpose(1, 0, 2),
+                             np.zeros((1, c.H_kv, c.D), np.uint16)])
+        vn = np.concatenate([c.v_pool[:, phys, :].transpose(1, 0, 2),
+                             np.zeros((1, c.H_kv, c.D), np.uint16)])
+        pt = c.page_table
+    vp0 = kp0.copy() if cfg != 2 else c.v_pool
+    kr, vr = oracle.append_pages(kp0, vp0, P, ps, pt, bi, ip, kn, vn)
+    kd, vd = dev_bf16(kp0), dev_bf16(vp0)
+    pkv.paged_kv_append(kd, vd, dev_i32(pt), dev_i32(bi), dev_i32(ip), dev_bf16(kn), dev_bf16(vn),
+                        page_size=ps)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(kd), kr)
+    assert np.array_equal(host_bits(vd), vr)
+
+
+def test_append_skips_and_invalid_entries():
+    """Slot 0, unmapped blocks (page 0), out-of-range slot/block/page: nothing written."""
+    _print_case("append skips")
+    H_kv, D, ps, P = 2, 64, 16, 12
+    pt = np.zeros((4, 3), np.int32)
+    pt[1] = [3, 0, 7]
+    pt[2] = [5, 11, 99]      # 99 is not a page of this pool
+    pt[3] = [-4, 2, 1]       # negative page id
+    bi = np.array([1, 1, 1, 0, 2, 2, 2, 4, 3, 3, -1, 1], np.int32)
+    ip = np.array([0, 17, 40, 5, 3, 20, 33, 0, 1, 20, 0, 48], np.int32)
+    rng = np.random.default_rng(5)
+    kn = f32_to_bf16_bits(rng.standard_normal((len(bi), H_kv, D), dtype=np.float32))
+    vn = f32_to_bf16_bits(rng.standard_normal((len(bi), H_kv, D), dtype=np.float32))
+    kp0 = np.full((H_kv, P * ps, D), BF16_NAN, np.uint16)
+    kr, vr = oracle.append_pages(kp0, kp0, P, ps, pt, bi, ip, kn, vn)
+    kd, vd = dev_bf16(kp0), dev_bf16(kp0)
+    pkv.paged_kv_append(kd, vd, dev_i32(pt), dev_i32(bi), dev_i32(ip), dev_bf16(kn), dev_bf16(vn),
+                        page_size=ps)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(kd), kr) and np.array_equal(host_bits(vd), vr)
+    assert np.all(host_bits(kd)[:, :ps] == BF16_NAN)
+
+
+# ----------------------------------------------------------------------------- decode
+SPLITS = [1, 2, 3, 7, 0]
+MODES = {"detect": 0, "walk": pkv.PKV_F_NO_CONTIG_DETECT}
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+@pytest.mark.parametrize("splits", SPLITS)
+@pytest.mark.parametrize("mode", list(MODES))
+def test_decode_parity(cfg, splits, mode):
+    _print_case(f"decode cfg{cfg} splits={splits} mode={mode}")
+    if cfg == 4 and mode == "walk" and splits in (3, 7):
+        pytest.skip("covered by the other split counts")
+    d = _dev(cfg)
+    _, _, out_ref, lse_ref = _ref(cfg)
+    out, lse = d.decode(num_splits=splits, flags=MODES[mode])
+    torch.cuda.synchronize()
+    check_close(out, lse, out_ref, lse_ref, f"cfg{cfg}/S{splits}/{mode}")
+
+
+def test_decode_assume_contiguous_bucketed():
+    """The caller's contiguity promise (sequential pages) gives the same result."""
+    _print_case("decode cfg3 assume-contiguous")
+    assert _case(3).contiguous
+    d = _dev(3)
+    _, _, out_ref, lse_ref = _ref(3)
+    for S in (1, 2, 0):
+        out, lse = d.decode(num_splits=S, flags=pkv.PKV_F_ASSUME_CONTIGUOUS)
+        torch.cuda.synchronize()
+        check_close(out, lse, out_ref, lse_ref, f"assume/S{S}")
+
+
+def test_decode_padding_rows_exact():
+    """Padding rows: exactly +0.0 and -inf, never NaN, with NaN in page 0 and slot 0."""
+    _print_case("decode padding rows")
+    d = _dev(3)
+    for S in (1, 2, 5):
+        out, lse = d.decode(num_splits=S)
+        torch.cuda.synchronize()
+        ob = host_bits(out)
+        lh = lse.cpu().numpy()
+        pad = np.nonzero(_case(3).batch_idx == 0)[0]
+        assert len(pad) == 14
+        assert np.all(ob[pad] == 0)          # +0.0 bit pattern
+        assert np.all(np.isneginf(lh[pad]))
+
+
+def test_decode_deterministic():
+    _print_case("decode determinism")
+    d = _dev(2)
+    for S in (1, 3):
+        o1, l1 = d.decode(num_splits=S)
+        o2, l2 = d.decode(num_splits=S)
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+        assert torch.equal(l1, l2)
+
+
+def _small_case(seed, H_q, H_kv, D, ps, lens, layout, slots=None, num_pages=None):
+    B = len(lens)
+    slots = slots if slots is not None else list(range(1, B + 1))
+    need = sum(-(-n // ps) for n, s in zip(lens, slots) if s)
+    mb = max([-(-n // ps) for n in lens] + [1])
+    return make_decode_case(name="small", seed=seed, H_q=H_q, H_kv=H_kv, D=D, page_size=ps,
+                            num_pages=num_pages or need + 3, num_slots=max(slots) + 1,
+                            max_blocks=mb, row_slots=slots, row_lens=lens, layout=layout,
+                            fill="nan")
+
+
+SMALL = [
+    # (seed, H_q, H_kv, D, ps, lens, layout)
+    (31, 8, 8, 128, 16, [1, 15, 16, 17, 31, 32, 33, 200], "shuffled"),      # G = 1
+    (32, 16, 2, 128, 32, [1, 63, 64, 65, 500], "shuffled"),                  # G = 8
+    (33, 16, 1, 64, 64, [1, 2, 127, 128, 129, 640], "shuffled"),             # G = 16
+    (34, 12, 4, 64, 16, [5, 96, 33, 1000], "sequential"),                    # G = 3
+    (35, 32, 8, 128, 256, [255, 256, 257, 2048], "shuffled"),                # big pages
+    (36, 32, 8, 128, 16, [16 * 40, 16 * 40 - 1, 16 * 70 + 3], "shuffled"),   # > 64 blocks
+]
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=[f"seed{s[0]}" for s in SMALL])
+@pytest.mark.parametrize("splits", [1, 2, 5, 0])
+def test_decode_edge_shapes(spec, splits):
+    seed, H_q, H_kv, D, ps, lens, layout = spec
+    _print_case(f"decode small seed={seed} splits={splits}")
+    c = _small_case(seed, H_q, H_kv, D, ps, lens, layout)
+    out_ref, lse_ref = oracle.decode_case(c)
+    d = _Dev(c)
+    for mode in MODES.values():
+        out, lse = d.decode(num_splits=splits, flags=mode)
+        torch.cuda.synchronize()
+        check_close(out, lse, out_ref, lse_ref, f"seed{seed}/S{splits}/flags{mode}")
+
+
+def test_decode_kv_len_zero_and_empty_splits():
+    """kv_len = 0 rows and splits that get no keys return (+0, -inf)."""
+    _print_case("decode kv_len 0")
+    c = _small_case(41, 8, 2, 128, 32, [0, 40, 3, 0], "shuffled")
+    out_ref, lse_ref = oracle.decode_case(c)
+    d = _Dev(c)
+    for S in (1, 4, 9):
+        out, lse = d.decode(num_splits=S)
+        torch.cuda.synchronize()
+        check_close(out, lse, out_ref, lse_ref, f"kvlen0/S{S}")
+        ob = host_bits(out)
+        assert np.all(ob[[0, 3]] == 0)
+
+
+def test_decode_needles():
+    """A dominating key at page edges and at n-1 is found; one at position n is ignored."""
+    _print_case("decode needles")
+    ps, n = 16, 70
+    positions = sorted({p for b in range(0, n, ps) for p in (b, min(b + ps - 1, n - 1))} | {n - 1})
+    targets = positions + [n]
+    c = _small_case(42, 8, 2, 64, ps, [n] * len(targets), "shuffled")
+    G = c.H_q // c.H_kv
+    for r, jstar in enumerate(targets):
+        for g in range(c.H_kv):
+            c.q[r, g * G:(g + 1) * G] = c.q[r, g * G]
+            phys = int(c.page_table[c.batch_idx[r], jstar // ps]) * ps + jstar % ps
+            c.k_pool[g, phys] = f32_to_bf16_bits(8.0 * bf16_bits_to_f32(c.q[r, g * G]))
+            if jstar >= n:
+                c.v_pool[g, phys] = f32_to_bf16_bits(np.full(c.D, 5.0, np.float32))
+    out_ref, lse_ref = oracle.decode_case(c)
+    d = _Dev(c)
+    for S in (1, 3):
+        out, lse = d.decode(num_splits=S)
+        torch.cuda.synchronize()
+        check_close(out, lse, out_ref, lse_ref, f"needles/S{S}")
+        o = bf16_bits_to_f32(host_bits(out))
+        assert np.abs(o[-1] - 5.0).min() > 1.0   # key n never admitted
+
+
+def test_decode_shape_sequence():
+    """Small, then large, then medium batches in one process (no shape specialisation)."""
+    _print_case("decode shape sequence")
+    for cfg in (1, 4, 2):
+        d = _dev(cfg)
+        _, _, out_ref, lse_ref = _ref(cfg)
+        out, lse = d.decode()
+        torch.cuda.synchronize()
+        check_close(out, lse, out_ref, lse_ref, f"seq cfg{cfg}")
+
+
+def test_prefill_decode_consistency_through_pages():
+    """Append a document's K/V into shuffled pages, decode its last query: equals the
+    oracle's prefill last row (decode side on the GPU)."""
+    _print_case("prefill->decode consistency")
+    pc = make_prefill_case(name="p11g", seed=43, doc_lens=[9, 130, 1, 257, 64], H_q=32, H_kv=8,
+                           D=128, page_size=128, num_pages=16, max_blocks=3)
+    out_ref, lse_ref = oracle.prefill_case(pc)
+    kd = dev_bf16(np.full((pc.H_kv, pc.num_pages * pc.page_size, pc.D), BF16_NAN, np.uint16))
+    vd = kd.clone()
+    pt = dev_i32(pc.page_table)
+    pkv.paged_kv_append(kd, vd, pt, dev_i32(pc.batch_idx), dev_i32(pc.input_pos), dev_bf16(pc.k),
+                        dev_bf16(pc.v), page_size=pc.page_size)
+    last = pc.cu_seqlens[1:] - 1
+    slots = np.arange(1, pc.n_docs + 1, dtype=np.int32)
+    lens = pc.doc_lens().astype(np.int32)
+    for S in (1, 2):
+        out, lse = pkv.paged_decode_attn(dev_bf16(pc.q[last]), kd, vd, pt, dev_i32(slots),
+                                         dev_i32(lens), page_size=pc.page_size,
+                                         scale=float(pc.scale), max_kv_len=int(lens.max()),
+                                         num_splits=S)
+        torch.cuda.synchronize()
+        check_close(out, lse, out_ref[last], lse_ref[last], f"p11/S{S}")
+    assert math.isfinite(float(lse.min()))

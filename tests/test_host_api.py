@@ -1,0 +1,122 @@
+"""CPU-only checks of the C ABI: the library loads, exports what include/pkv.h
+declares, and rejects bad arguments on the host before any HIP call."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+LIB = os.path.join(ROOT, "paged_kv_attention_23_amd", "libpkv.so")
+
+from paged_kv_attention_23_amd import _binding as B  # noqa: E402
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        import __graft_entry__
+        __graft_entry__.build()
+    return B.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert set(names) >= {"paged_kv_append", "paged_decode_attn", "packed_prefill_attn",
+                          "paged_decode_workspace_size", "paged_decode_num_splits",
+                          "pkv_last_error"}
+    raw = ctypes.CDLL(LIB)
+    for n in names:
+        assert hasattr(raw, n), f"{n} declared in pkv.h but not exported"
+
+
+def test_header_constants_parsed():
+    assert B._C["PKV_OK"] == 0 and B._C["PKV_E_HIP"] == -6
+    assert B.PKV_F_ASSUME_CONTIGUOUS == 1 and B.PKV_F_NO_CONTIG_DETECT == 2
+    assert B.PKV_MAX_SPLITS == 64
+
+
+FAKE = 0x100000  # a 16-byte-aligned non-null value: only ever seen by host checks
+
+
+def _decode(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, num_pages=8, page_size=16, H_kv=2, D=128, pt=FAKE,
+             num_slots=3, max_blocks=4, bi=FAKE, kl=FAKE, batch=2, H_q=4, scale=0.125,
+             max_kv_len=64, splits=1, flags=0, ws=0, ws_bytes=0, out=FAKE, lse=FAKE, stream=0)
+    a.update(kw)
+    return lib.paged_decode_attn(a["q"], a["k"], a["v"], a["num_pages"], a["page_size"], a["H_kv"],
+                                 a["D"], a["pt"], a["num_slots"], a["max_blocks"], a["bi"], a["kl"],
+                                 a["batch"], a["H_q"], a["scale"], a["max_kv_len"], a["splits"],
+                                 a["flags"], a["ws"], a["ws_bytes"], a["out"], a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(D=96), -2, "head_dim"),
+    (dict(page_size=24), -2, "page_size"),
+    (dict(page_size=8), -2, "page_size"),
+    (dict(H_q=5), -2, "multiple"),
+    (dict(H_q=34, H_kv=2), -2, "16 query heads"),
+    (dict(batch=-1), -2, "batch"),
+    (dict(num_pages=0), -2, "num_pages"),
+    (dict(max_blocks=0), -2, "max_blocks"),
+    (dict(scale=float("nan")), -2, "scale"),
+    (dict(splits=65), -5, "num_splits"),
+    (dict(splits=-1), -5, "num_splits"),
+    (dict(flags=8), -2, "flag"),
+    (dict(q=0), -1, "NULL"),
+    (dict(lse=0), -1, "NULL"),
+    (dict(q=FAKE + 2), -3, "aligned"),
+    (dict(out=FAKE + 8), -3, "aligned"),
+    (dict(kl=FAKE + 2), -3, "aligned"),
+    (dict(splits=2), -4, "workspace"),
+    (dict(splits=2, ws=FAKE, ws_bytes=100), -4, "workspace"),
+    (dict(splits=2, ws=FAKE + 4, ws_bytes=1 << 20), -3, "workspace"),
+])
+def test_decode_rejects(lib, kw, code, msg):
+    rc = _decode(lib, **kw)
+    assert rc == code, (rc, B.last_error())
+    assert msg in B.last_error()
+
+
+def test_decode_empty_batch_is_noop(lib):
+    assert _decode(lib, batch=0, q=0, k=0, v=0, pt=0, bi=0, kl=0, out=0, lse=0) == 0
+
+
+def test_append_checks(lib):
+    f = lib.paged_kv_append
+    assert f(0, 0, 8, 16, 2, 128, 0, 3, 4, 0, 0, 0, 0, 0, 0) == 0          # no tokens: no-op
+    assert f(FAKE, FAKE, 8, 16, 2, 128, FAKE, 3, 4, FAKE, FAKE, -1, FAKE, FAKE, 0) == -2
+    assert f(FAKE, FAKE, 8, 12, 2, 128, FAKE, 3, 4, FAKE, FAKE, 1, FAKE, FAKE, 0) == -2
+    assert f(FAKE, 0, 8, 16, 2, 128, FAKE, 3, 4, FAKE, FAKE, 1, FAKE, FAKE, 0) == -1
+    assert f(FAKE, FAKE, 8, 16, 2, 128, FAKE, 3, 4, FAKE, FAKE, 1, FAKE + 2, FAKE, 0) == -3
+    assert f(FAKE, FAKE, 8, 16, 2, 100, FAKE, 3, 4, FAKE, FAKE, 1, FAKE, FAKE, 0) == -2
+    assert "head_dim" in B.last_error()
+
+
+def test_prefill_checks(lib):
+    f = lib.packed_prefill_attn
+    assert f(0, 0, 0, 0, 0, 0, 32, 8, 128, 0.1, 0, 0, 0) == 0               # empty: no-op
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 10, 32, 8, 64, 0.1, FAKE, FAKE, 0) == -2
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 10, 30, 8, 128, 0.1, FAKE, FAKE, 0) == -2
+    assert f(FAKE, FAKE, FAKE, FAKE, 0, 10, 32, 8, 128, 0.1, FAKE, FAKE, 0) == -2
+    assert f(FAKE, 0, FAKE, FAKE, 1, 10, 32, 8, 128, 0.1, FAKE, FAKE, 0) == -1
+    assert f(FAKE, FAKE, FAKE, FAKE + 1, 1, 10, 32, 8, 128, 0.1, FAKE, FAKE, 0) == -3
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, -5, 32, 8, 128, 0.1, FAKE, FAKE, 0) == -2
+
+
+def test_workspace_size(lib):
+    ws = lib.paged_decode_workspace_size
+    assert ws(4, 32, 128, 1) == 0 and ws(4, 32, 128, 0) == 0
+    rows = 3 * 2 * 4
+    o_bytes = (rows * 128 * 4 + 255) // 256 * 256
+    assert ws(2, 4, 128, 3) == o_bytes + rows * 4
+    assert ws(0, 4, 128, 3) == 0
