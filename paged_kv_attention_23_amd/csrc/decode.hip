@@ -51,10 +51,12 @@ struct DecGeom {
 
 // Where the keys of one (row, KV head) unit live.  Page ids of 64
 // consecutive logical blocks starting at wbase sit one per lane in pwin, so
-// a lookup is a single v_readlane with a wave-uniform index.
+// a lookup is a single v_readlane with a wave-uniform index.  The window is
+// loaded once per segment of at most 64 blocks (outside the tile loop, with
+// an explicit wait), so the loop never waits on it.
 struct RowCtx {
   const int32_t *pt_row;  // page-table row of the slot
-  int64_t contig_base;    // pool row of logical key 0 when contig
+  int contig_base;        // pool row of logical key 0 when contig
   int page_shift, num_pages, max_blocks, hi;
   int wbase;              // first logical block held in pwin
   int pwin;               // per lane: page id of block wbase + lane
@@ -65,49 +67,49 @@ __device__ __forceinline__ void load_window(RowCtx &c, int wbase, int lane) {
   c.wbase = wbase;
   const int b = wbase + lane;
   c.pwin = (b < c.max_blocks) ? c.pt_row[b] : 0;
+  __builtin_amdgcn_s_waitcnt(0);  // the window is ready before any tile uses it
 }
 
 // Pool row of the first key of a 16-key block (key0 is a multiple of 16 and
 // page_size >= 16, so the block sits in one page).  Blocks wholly past the
-// valid keys point at row 0, which always exists; their values are masked.
-__device__ __forceinline__ int64_t block_row(const RowCtx &c, int key0) {
-  if (key0 >= c.hi) return 0;
-  if (c.contig) return c.contig_base + key0;
+// valid keys map to row 0, which always exists: tiles past the end are still
+// loaded (so every pipeline step issues the same number of loads) but they
+// all hit the same cached rows and are never used.
+__device__ __forceinline__ uint32_t block_row(const RowCtx &c, int key0) {
+  if (key0 >= c.hi) return 0u;
+  if (c.contig) return (uint32_t)(c.contig_base + key0);
   int page = __builtin_amdgcn_readlane(c.pwin, (key0 >> c.page_shift) - c.wbase);
   page = min(max(page, 0), c.num_pages - 1);
-  return ((int64_t)page << c.page_shift) + (key0 & ((1 << c.page_shift) - 1));
+  return ((uint32_t)page << c.page_shift) + (uint32_t)(key0 & ((1 << c.page_shift) - 1));
 }
 
-// Make sure both blocks of the tile starting at kt are inside the window.
-__device__ __forceinline__ void ensure_window(RowCtx &c, int kt, int lane) {
-  if (c.contig) return;
-  const int last = min(kt + kTileKeys, c.hi) - 1;
-  if ((last >> c.page_shift) - c.wbase >= kWave) load_window(c, kt >> c.page_shift, lane);
-}
-
+// K rows of a 32-key tile as QK A-operands.  kbase is the KV head's plane;
+// offsets are 32-bit (a head plane is below 4 GiB).
 template <int D>
-__device__ __forceinline__ void load_k(u32x4 (&k)[2][D / 32], const RowCtx &c,
-                                       const uint16_t *kbase, int kt, int lane) {
+__device__ __forceinline__ void load_k(u32x4 (&k)[2][D / 32], const RowCtx &c, const char *kbase,
+                                       int kt, int lane) {
   const int hl = lane & 15, lg = lane >> 4;
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
-    const uint16_t *kr = kbase + (block_row(c, kt + 16 * b) + hl) * D + 8 * lg;
+    const uint32_t off = (block_row(c, kt + 16 * b) + hl) * (2u * D) + 16u * lg;
 #pragma unroll
-    for (int ch = 0; ch < D / 32; ++ch) k[b][ch] = *reinterpret_cast<const u32x4 *>(kr + 32 * ch);
+    for (int ch = 0; ch < D / 32; ++ch)
+      k[b][ch] = *reinterpret_cast<const u32x4 *>(kbase + off + 64u * ch);
   }
 }
 
 template <int D>
-__device__ __forceinline__ void load_v(u32x4 (&v)[D / 16], const RowCtx &c, const uint16_t *vbase,
+__device__ __forceinline__ void load_v(u32x4 (&v)[D / 16], const RowCtx &c, const char *vbase,
                                        int kt, int lane) {
   using Gm = DecGeom<D>;
-  const int64_t row0 = block_row(c, kt), row1 = block_row(c, kt + 16);
+  const uint32_t row0 = block_row(c, kt), row1 = block_row(c, kt + 16);
+  const uint32_t lane_off = (uint32_t)(lane / Gm::kLanesPerRow) * (2u * D) +
+                            (uint32_t)(lane % Gm::kLanesPerRow) * 16u;
 #pragma unroll
   for (int i = 0; i < Gm::kVLoads; ++i) {
-    const int key = i * Gm::kKeysPerLoad + lane / Gm::kLanesPerRow;  // key within the tile
-    const int64_t rb = (i * Gm::kKeysPerLoad < 16) ? row0 : row1;     // a load never straddles blocks
-    v[i] = *reinterpret_cast<const u32x4 *>(vbase + (rb + (key & 15)) * D +
-                                            (lane % Gm::kLanesPerRow) * 8);
+    const int first = i * Gm::kKeysPerLoad;                 // first key of this load in the tile
+    const uint32_t rb = (first < 16) ? row0 : row1;         // a load never straddles blocks
+    v[i] = *reinterpret_cast<const u32x4 *>(vbase + (rb + (first & 15)) * (2u * D) + lane_off);
   }
 }
 
@@ -255,6 +257,19 @@ void decode_kernel(DecodeArgs a) {
   const int hl = lane & 15, lg = lane >> 4;
   const int G = a.G;
 
+  // Q^T as B operands: column hl = query head g*G + hl (zero past G).  Issued
+  // first: it does not depend on the slot, so it overlaps the row lookups.
+  bf16x8 qop[Gm::kDChunks];
+  {
+    const uint16_t *qr = a.q + ((int64_t)r * a.H_q + g * G + hl) * D + 8 * lg;
+#pragma unroll
+    for (int ch = 0; ch < Gm::kDChunks; ++ch) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (hl < G) w = *reinterpret_cast<const u32x4 *>(qr + 32 * ch);
+      qop[ch] = as_bf16x8(w);
+    }
+  }
+
   const int s = a.batch_idx[r];
   int n = a.kv_len[r];
   n = min(n, a.max_blocks << a.page_shift);
@@ -290,23 +305,11 @@ void decode_kernel(DecodeArgs a) {
       }
     }
     c.contig = ok;
-    c.contig_base = ((int64_t)first - blk_lo) << a.page_shift;
+    c.contig_base = (first - blk_lo) << a.page_shift;
   }
 
-  const uint16_t *kbase = a.k_pool + (int64_t)g * a.plane_rows * D;
-  const uint16_t *vbase = a.v_pool + (int64_t)g * a.plane_rows * D;
-
-  // Q^T as B operands: column hl = query head g*G + hl (zero past G).
-  bf16x8 qop[Gm::kDChunks];
-  {
-    const uint16_t *qr = a.q + ((int64_t)r * a.H_q + g * G + hl) * D + 8 * lg;
-#pragma unroll
-    for (int ch = 0; ch < Gm::kDChunks; ++ch) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (hl < G) w = *reinterpret_cast<const u32x4 *>(qr + 32 * ch);
-      qop[ch] = as_bf16x8(w);
-    }
-  }
+  const char *kbase = reinterpret_cast<const char *>(a.k_pool + (int64_t)g * a.plane_rows * D);
+  const char *vbase = reinterpret_cast<const char *>(a.v_pool + (int64_t)g * a.plane_rows * D);
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 o[Gm::kDBlocks];
@@ -314,38 +317,40 @@ void decode_kernel(DecodeArgs a) {
   for (int t = 0; t < Gm::kDBlocks; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   char *vlds = smem + wave * Gm::kVBytes;
-  const int ntiles = (hi - lo + kTileKeys - 1) / kTileKeys;
 
-  // Software pipeline: K of the next tile goes to the other register set and
-  // V of the next tile to the staging registers while the current tile is
-  // computed; two K sets, one V set (staged to LDS first thing each step).
+  // The key range is walked in segments of at most 64 blocks (one page-id
+  // window each; a single segment when the pages are contiguous).  Within a
+  // segment, a software pipeline keeps the next tile's K (other register set)
+  // and V (staging registers) in flight while the current tile is computed.
   u32x4 ka[2][D / 32], kb[2][D / 32], vr[D / 16];
-  int t = wave;
-  if (t < ntiles) {
-    ensure_window(c, lo + t * kTileKeys, lane);
-    load_v<D>(vr, c, vbase, lo + t * kTileKeys, lane);
-    load_k<D>(ka, c, kbase, lo + t * kTileKeys, lane);
-  }
-  while (t < ntiles) {
-    store_v<D>(vr, vlds, lo + t * kTileKeys, hi, lane);
-    int tn = t + kDecWaves;
-    if (tn < ntiles) {
-      ensure_window(c, lo + tn * kTileKeys, lane);
-      load_v<D>(vr, c, vbase, lo + tn * kTileKeys, lane);
-      load_k<D>(kb, c, kbase, lo + tn * kTileKeys, lane);
+  for (int seg_lo = lo; seg_lo < hi;) {
+    const int seg_blk = seg_lo >> a.page_shift;
+    const int seg_hi = c.contig ? hi
+                                : (int)min((int64_t)hi, ((int64_t)seg_blk + kWave) << a.page_shift);
+    if (!c.contig && seg_blk != c.wbase) load_window(c, seg_blk, lane);
+    c.hi = seg_hi;
+    const int ntiles = (seg_hi - seg_lo + kTileKeys - 1) / kTileKeys;
+    int t = wave;
+    load_v<D>(vr, c, vbase, seg_lo + t * kTileKeys, lane);
+    load_k<D>(ka, c, kbase, seg_lo + t * kTileKeys, lane);
+    while (t < ntiles) {
+      store_v<D>(vr, vlds, seg_lo + t * kTileKeys, seg_hi, lane);
+      int tn = t + kDecWaves;
+      load_v<D>(vr, c, vbase, seg_lo + tn * kTileKeys, lane);
+      load_k<D>(kb, c, kbase, seg_lo + tn * kTileKeys, lane);
+      compute_tile<D>(ka, seg_lo + t * kTileKeys, seg_hi, vlds, qop, m_run, l_run, o,
+                      a.scale_log2, lane);
+      t = tn;
+      if (t >= ntiles) break;
+      store_v<D>(vr, vlds, seg_lo + t * kTileKeys, seg_hi, lane);
+      tn = t + kDecWaves;
+      load_v<D>(vr, c, vbase, seg_lo + tn * kTileKeys, lane);
+      load_k<D>(ka, c, kbase, seg_lo + tn * kTileKeys, lane);
+      compute_tile<D>(kb, seg_lo + t * kTileKeys, seg_hi, vlds, qop, m_run, l_run, o,
+                      a.scale_log2, lane);
+      t = tn;
     }
-    compute_tile<D>(ka, lo + t * kTileKeys, hi, vlds, qop, m_run, l_run, o, a.scale_log2, lane);
-    t = tn;
-    if (t >= ntiles) break;
-    store_v<D>(vr, vlds, lo + t * kTileKeys, hi, lane);
-    tn = t + kDecWaves;
-    if (tn < ntiles) {
-      ensure_window(c, lo + tn * kTileKeys, lane);
-      load_v<D>(vr, c, vbase, lo + tn * kTileKeys, lane);
-      load_k<D>(ka, c, kbase, lo + tn * kTileKeys, lane);
-    }
-    compute_tile<D>(kb, lo + t * kTileKeys, hi, vlds, qop, m_run, l_run, o, a.scale_log2, lane);
-    t = tn;
+    seg_lo = seg_hi;
   }
 
   // Combine the 4 waves through LDS (the merge area reuses the V tiles).

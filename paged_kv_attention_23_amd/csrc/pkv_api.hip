@@ -47,6 +47,8 @@ int check_pool(int32_t num_pages, int32_t page_size, int32_t num_kv_heads, int32
                 max_blocks);
   if ((int64_t)max_blocks * page_size > INT32_MAX)
     return fail(PKV_E_SHAPE, "max_blocks*page_size exceeds 2^31-1 keys");
+  if ((int64_t)num_pages * page_size * head_dim * 2 > (int64_t)UINT32_MAX)
+    return fail(PKV_E_SHAPE, "one KV head plane (num_pages*page_size*head_dim*2 bytes) must be below 4 GiB");
   return PKV_OK;
 }
 
@@ -75,10 +77,13 @@ constexpr int kTileKeys = 32;
 constexpr int kMinSplitKeys = 256;
 
 int32_t auto_splits(int32_t batch, int32_t num_kv_heads, int32_t max_kv_len, int cus) {
+  // One workgroup per (row, KV head) already fills the chip when there are at
+  // least as many units as compute units; splitting then only adds the merge
+  // pass.  Below that, split so that roughly one unit lands on every CU,
+  // keeping at least kMinSplitKeys keys per split.
   const int64_t units = (int64_t)batch * num_kv_heads;
-  if (units <= 0 || max_kv_len <= 0) return 1;
-  const int64_t target = 4LL * cus;  // workgroups wanted in flight
-  int64_t s = (target + units - 1) / units;
+  if (units <= 0 || max_kv_len <= 0 || units >= cus) return 1;
+  int64_t s = (cus + units / 2) / units;
   const int64_t by_len = max_kv_len / kMinSplitKeys;
   if (s > by_len) s = by_len;
   if (s > PKV_MAX_SPLITS) s = PKV_MAX_SPLITS;
@@ -226,6 +231,9 @@ int packed_prefill_attn(const void *q, const void *k, const void *v, const int32
   if (num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
     return fail(PKV_E_SHAPE, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
                 num_q_heads, num_kv_heads);
+  if (num_q_heads / num_kv_heads > 16)
+    return fail(PKV_E_SHAPE, "at most 16 query heads per KV head are supported (got %d)",
+                num_q_heads / num_kv_heads);
   if (!(scale == scale) || isinf(scale)) return fail(PKV_E_SHAPE, "scale must be finite");
   if (total_len == 0) return PKV_OK;
   if (num_docs == 0) return fail(PKV_E_SHAPE, "total_len > 0 needs at least one document");

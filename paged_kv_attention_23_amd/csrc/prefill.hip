@@ -1,14 +1,285 @@
-// Packed document-causal prefill (placeholder until the matrix-core kernel lands).
+// Packed document-causal prefill attention on the bf16 matrix cores.
+//
+// What is computed is the prefill of the qwen3_flex_inference.py page:
+// prompts packed into one sequence, each token attending to the tokens of
+// its own document up to itself, with GQA and scale.  Documents are the row
+// ranges [cu_seqlens[d], cu_seqlens[d+1]).
+//
+// Decomposition (MI355X-specific):
+//  * A workgroup owns one query tile of one document and one KV head: 128
+//    (query head, query row) pairs, i.e. QT = 128 / G query rows for all G
+//    query heads that share the KV head, so each K/V tile staged in LDS serves
+//    G heads.  Tiles never straddle documents.
+//  * blockIdx enumerates (tile, KV head) with the KV head fastest; workgroups
+//    are dealt round-robin to the 8 XCDs, so with 8 KV heads each XCD serves
+//    one head and the query tiles of a document re-read its K/V from that
+//    XCD's L2.  Tiles are ordered longest first (largest key range first).
+//  * Each of the 4 waves owns 32 of the 128 rows (two 16-column blocks).
+//    Scores are computed transposed, S^T[key][row] = K Q^T, so the score
+//    layout is directly the B operand P^T of O^T = V^T P^T (the same scheme
+//    as the decode kernel); V^T operands come from 16-byte LDS reads of V
+//    rows, with the head_dim order permuted consistently.
+//  * K/V stages of 64 keys are double buffered in LDS (row stride padded by
+//    16 bytes so both the K-operand and V reads spread over all banks); the
+//    next stage's global loads are in flight while the current one is used.
+//  * Online softmax in base 2 in fp32; causal masking only on stages that
+//    reach the diagonal.
+#include <math.h>
+
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
 namespace pkv {
 
+constexpr int kPfD = 128;
+constexpr int kPfWaves = 4;
+constexpr int kPfThreads = kPfWaves * kWave;
+constexpr int kPfRows = 128;                         // (head, query) rows per workgroup
+constexpr int kPfBN = 64;                            // keys per LDS stage
+constexpr int kPfRowStride = 2 * kPfD + 16;          // bytes per key row in LDS
+constexpr int kPfTileBytes = kPfBN * kPfRowStride;   // one K or V stage
+constexpr int kPfSmem = 2 * 2 * kPfTileBytes;        // 2 stages x (K, V)
+constexpr int kPfLoads = kPfBN * (2 * kPfD / 16) / kPfThreads;  // 16-byte pieces per thread per tensor
+
+struct PfTile {
+  int doc_start, q_lo, q_hi;
+};
+
+// Tile number -> (document, query tile), longest key range first: level j
+// holds query tile j of every document with more than j tiles, levels in
+// descending j, documents in order within a level.  Every wave computes this
+// redundantly from cu_seqlens (a few loads that hit in cache).
+__device__ bool find_tile(const int32_t *cu, int num_docs, int QT, int tile, int lane, PfTile &out) {
+  // longest document, in tiles
+  int jmax = 0;
+  for (int d0 = 0; d0 < num_docs; d0 += kWave) {
+    const int d = d0 + lane;
+    int t = 0;
+    if (d < num_docs) t = (cu[d + 1] - cu[d] + QT - 1) / QT;
+    for (int m = 1; m < kWave; m <<= 1) t = max(t, __shfl_xor(t, m, kWave));
+    jmax = max(jmax, t);
+  }
+  for (int j = jmax - 1; j >= 0; --j) {
+    for (int d0 = 0; d0 < num_docs; d0 += kWave) {
+      const int d = d0 + lane;
+      bool has = false;
+      if (d < num_docs) has = (cu[d + 1] - cu[d]) > j * QT;
+      const uint64_t mask = __ballot(has);
+      const int cnt = __popcll(mask);
+      if (tile < cnt) {
+        // position of the tile-th set bit
+        uint64_t m = mask;
+        for (int k = 0; k < tile; ++k) m &= m - 1;
+        const int dd = d0 + __builtin_ctzll(m);
+        out.doc_start = cu[dd];
+        out.q_lo = cu[dd] + j * QT;
+        out.q_hi = min(cu[dd + 1], out.q_lo + QT);
+        return true;
+      }
+      tile -= cnt;
+    }
+  }
+  return false;
+}
+
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void prefill_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[kPfSmem];
+  constexpr int D = kPfD;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int hl = lane & 15, lg = lane >> 4;
+  const int g = blockIdx.x % a.H_kv;
+  const int tile = blockIdx.x / a.H_kv;
+  const int G = a.G;
+  const int QT = kPfRows / G;  // query rows per tile
+
+  PfTile tl;
+  if (!find_tile(a.cu_seqlens, a.num_docs, QT, tile, lane, tl)) return;  // uniform
+  const int k_lo = tl.doc_start, k_hi = tl.q_hi;
+
+  // Rows of this wave: column block qb, column hl -> tile row R.
+  int col_head[2], col_q[2];
+  bool col_ok[2];
+  bf16x8 qop[2][D / 32];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int R = 32 * wave + 16 * qb + hl;
+    const int hh = R / QT, qq = tl.q_lo + R % QT;
+    col_ok[qb] = (hh < G) && (qq < tl.q_hi);
+    col_head[qb] = g * G + min(hh, G - 1);
+    col_q[qb] = col_ok[qb] ? qq : k_lo - 1;  // unused columns mask every key
+    const uint16_t *qr = a.q + ((int64_t)col_q[qb] * a.H_q + col_head[qb]) * D + 8 * lg;
+#pragma unroll
+    for (int ch = 0; ch < D / 32; ++ch) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (col_ok[qb]) w = *reinterpret_cast<const u32x4 *>(qr + 32 * ch);
+      qop[qb][ch] = as_bf16x8(w);
+    }
+  }
+
+  // Cooperative stage loads: piece p = threadIdx.x + 256*i -> key row p/16, 16-byte column p%16.
+  const int64_t row_stride = (int64_t)a.H_kv * D;  // elements between consecutive tokens
+  const uint16_t *kg = a.k + (int64_t)g * D;
+  const uint16_t *vg = a.v + (int64_t)g * D;
+  u32x4 stk[kPfLoads], stv[kPfLoads];
+  auto load_stage = [&](int s) {
+#pragma unroll
+    for (int i = 0; i < kPfLoads; ++i) {
+      const int p = threadIdx.x + kPfThreads * i;
+      const int key = min(k_lo + s * kPfBN + (p >> 4), k_hi - 1);
+      const int64_t off = (int64_t)key * row_stride + (p & 15) * 8;
+      stk[i] = *reinterpret_cast<const u32x4 *>(kg + off);
+      stv[i] = *reinterpret_cast<const u32x4 *>(vg + off);
+    }
+  };
+  auto store_stage = [&](int s, int buf) {
+    char *kb = smem + buf * 2 * kPfTileBytes;
+    char *vb = kb + kPfTileBytes;
+#pragma unroll
+    for (int i = 0; i < kPfLoads; ++i) {
+      const int p = threadIdx.x + kPfThreads * i;
+      const bool live = k_lo + s * kPfBN + (p >> 4) < k_hi;
+      const int off = (p >> 4) * kPfRowStride + (p & 15) * 16;
+      *reinterpret_cast<u32x4 *>(kb + off) = live ? stk[i] : u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4 *>(vb + off) = live ? stv[i] : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  f32x4 o[2][D / 16];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) o[qb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nsteps = (k_hi - k_lo + kPfBN - 1) / kPfBN;
+  const int q_first = tl.q_lo;  // smallest query row of the tile
+  load_stage(0);
+  store_stage(0, 0);
+  __syncthreads();
+  for (int s = 0; s < nsteps; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < nsteps) load_stage(s + 1);
+    const char *kb = smem + buf * 2 * kPfTileBytes;
+    const char *vb = kb + kPfTileBytes;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {  // two 32-key halves of the stage
+      const int key0 = k_lo + s * kPfBN + 32 * h2;
+      if (key0 >= k_hi) break;  // uniform
+      // S^T blocks: keys key0 + 16*kb2 + (4*lg + i), columns qb.
+      f32x4 sc[2][2];
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        bf16x8 kop[D / 32];
+        const char *kr = kb + (32 * h2 + 16 * kb2 + hl) * kPfRowStride + 16 * lg;
+#pragma unroll
+        for (int ch = 0; ch < D / 32; ++ch) kop[ch] = as_bf16x8(*reinterpret_cast<const u32x4 *>(kr + 64 * ch));
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ch = 0; ch < D / 32; ++ch) acc = mfma16x16x32(kop[ch], qop[qb][ch], acc);
+          sc[kb2][qb] = acc;
+        }
+      }
+      const bool diag = key0 + 31 >= q_first;  // some key may lie past some query row
+      bf16x8 pop[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[i] = sc[0][qb][i] * a.scale_log2;
+          x[4 + i] = sc[1][qb][i] * a.scale_log2;
+        }
+        if (diag) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int key = key0 + (i < 4 ? 4 * lg + i : 16 + 4 * lg + (i - 4));
+            if (key > col_q[qb]) x[i] = -INFINITY;
+          }
+        }
+        float mt = x[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) mt = fmaxf(mt, x[i]);
+        mt = fmaxf(mt, shfl_xor_f(mt, 16));
+        mt = fmaxf(mt, shfl_xor_f(mt, 32));
+        const float m_new = fmaxf(m_run[qb], mt);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run[qb] - m_use);
+        float p[8], ps = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          p[i] = fast_exp2(x[i] - m_use);
+          ps += p[i];
+        }
+        l_run[qb] = l_run[qb] * alpha + ps;
+        m_run[qb] = m_new;
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) o[qb][t] *= alpha;
+        const u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                          pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+        pop[qb] = as_bf16x8(pw);
+      }
+      // V^T operands: lane reads V[key kappa(lg, e)][8*hl .. 8*hl+7]; step t
+      // uses head_dim d = 8*m + t for its row m.
+      uint32_t rv[8][4];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int kr = 32 * h2 + (e < 4 ? 4 * lg + e : 16 + 4 * lg + (e - 4));
+        const u32x4 w = *reinterpret_cast<const u32x4 *>(vb + kr * kPfRowStride + 16 * hl);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rv[e][j] = w[j];
+      }
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) {
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t a0 = rv[2 * j][t >> 1], a1 = rv[2 * j + 1][t >> 1];
+          w[j] = (t & 1) ? ((a0 >> 16) | (a1 & 0xffff0000u)) : ((a0 & 0xffffu) | (a1 << 16));
+        }
+        const bf16x8 vop = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) o[qb][t] = mfma16x16x32(vop, pop[qb], o[qb][t]);
+      }
+    }
+    if (s + 1 < nsteps) store_stage(s + 1, buf ^ 1);
+    __syncthreads();
+  }
+
+  // Normalise and write: lane holds O[row][d = 32*lg + 8*i + t] for t = 0..7.
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    float l = l_run[qb];
+    l += shfl_xor_f(l, 16);
+    l += shfl_xor_f(l, 32);
+    if (!col_ok[qb]) continue;
+    const float inv = (l > 0.f) ? 1.f / l : 0.f;
+    const int64_t rh = (int64_t)col_q[qb] * a.H_q + col_head[qb];
+    uint16_t *orow = a.out + rh * D + 32 * lg;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 w = {pack_bf16x2(o[qb][0][i] * inv, o[qb][1][i] * inv),
+                       pack_bf16x2(o[qb][2][i] * inv, o[qb][3][i] * inv),
+                       pack_bf16x2(o[qb][4][i] * inv, o[qb][5][i] * inv),
+                       pack_bf16x2(o[qb][6][i] * inv, o[qb][7][i] * inv)};
+      *reinterpret_cast<u32x4 *>(orow + 8 * i) = w;
+    }
+    if (lg == 0) a.lse[rh] = (l > 0.f) ? (m_run[qb] + log2f(l)) * kLn2 : -INFINITY;
+  }
+}
+
 hipError_t launch_prefill(const PrefillArgs &a, int32_t num_tiles_bound, hipStream_t stream) {
-  (void)a;
   (void)num_tiles_bound;
-  (void)stream;
-  return hipErrorNotSupported;
+  if (a.L == 0) return hipSuccess;
+  const int QT = kPfRows / a.G;
+  // Sum over documents of ceil(n_d / QT) is at most ceil(L / QT) + num_docs.
+  const int64_t tiles = ((int64_t)a.L + QT - 1) / QT + a.num_docs;
+  const int64_t blocks = tiles * a.H_kv;
+  hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)blocks), dim3(kPfThreads), 0, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace pkv

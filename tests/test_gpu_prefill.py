@@ -1,0 +1,108 @@
+"""GPU parity of packed_prefill_attn against the float64 oracle."""
+from __future__ import annotations
+
+import functools
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import BF16_NAN, make_case, make_prefill_case
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+import paged_kv_attention_23_amd as pkv  # noqa: E402
+from gpu_util import check_close, dev_bf16, dev_i32, host_bits  # noqa: E402
+
+
+def _run(pc):
+    out, lse = pkv.packed_prefill_attn(dev_bf16(pc.q), dev_bf16(pc.k), dev_bf16(pc.v),
+                                       dev_i32(pc.cu_seqlens), scale=float(pc.scale))
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@functools.lru_cache(maxsize=None)
+def _cfg5():
+    pc = make_case(5)
+    return pc, oracle.prefill_case(pc)
+
+
+def test_prefill_packed_64_docs():
+    """The 64-document packed workload (L ~ 18k, H_q=32, H_kv=8, D=128), every row."""
+    print("prefill cfg5", flush=True)
+    pc, (out_ref, lse_ref) = _cfg5()
+    out, lse = _run(pc)
+    check_close(out, lse, out_ref, lse_ref, "prefill cfg5")
+
+
+EDGE = [
+    # (seed, doc_lens, H_q, H_kv)
+    (51, [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129], 32, 8),     # G = 4, tile edges
+    (52, [0, 5, 0, 0, 70, 0], 8, 8),                                  # G = 1, empty documents
+    (53, [300, 1, 17], 16, 8),                                        # G = 2
+    (54, [200, 45, 9], 32, 4),                                        # G = 8
+    (55, [130, 7, 1], 16, 1),                                         # G = 16
+    (56, [1] * 40, 12, 4),                                            # G = 3 (rows not a power of two)
+    (57, [1000], 32, 8),                                              # one long document
+]
+
+
+@pytest.mark.parametrize("spec", EDGE, ids=[f"seed{s[0]}" for s in EDGE])
+def test_prefill_edge_shapes(spec):
+    seed, lens, H_q, H_kv = spec
+    print(f"prefill edge seed={seed}", flush=True)
+    pc = make_prefill_case(name="edge", seed=seed, doc_lens=lens, H_q=H_q, H_kv=H_kv, D=128,
+                           page_size=128, num_pages=64, max_blocks=8)
+    out_ref, lse_ref = oracle.prefill_case(pc)
+    out, lse = _run(pc)
+    check_close(out, lse, out_ref, lse_ref, f"prefill seed{seed}")
+
+
+def test_prefill_document_order_and_determinism():
+    """Permuting documents permutes rows bit for bit; repeated calls are bitwise equal."""
+    print("prefill permutation", flush=True)
+    pc = make_prefill_case(name="perm", seed=58, doc_lens=[70, 3, 129, 1, 64], H_q=32, H_kv=8,
+                           D=128, page_size=128, num_pages=16, max_blocks=2)
+    out, lse = _run(pc)
+    out2, lse2 = _run(pc)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16)) and torch.equal(lse, lse2)
+    order = [2, 4, 0, 3, 1]
+    cu = pc.cu_seqlens
+    idx = np.concatenate([np.arange(cu[d], cu[d + 1]) for d in order])
+    cu2 = np.concatenate([[0], np.cumsum([cu[d + 1] - cu[d] for d in order])]).astype(np.int32)
+    o3, l3 = pkv.packed_prefill_attn(dev_bf16(pc.q[idx]), dev_bf16(pc.k[idx]), dev_bf16(pc.v[idx]),
+                                     dev_i32(cu2), scale=float(pc.scale))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(o3), host_bits(out)[idx])
+    assert np.array_equal(l3.cpu().numpy(), lse.cpu().numpy()[idx])
+
+
+def test_prefill_then_decode_through_pages():
+    """Packed prefill of the 64 documents, their K/V appended into shuffled pages, and a
+    decode of each document's last query agree (both on the GPU)."""
+    print("prefill vs decode through pages", flush=True)
+    pc, (out_ref, lse_ref) = _cfg5()
+    out, lse = _run(pc)
+    kp = torch.full((pc.H_kv, pc.num_pages * pc.page_size, pc.D), BF16_NAN, dtype=torch.int16,
+                    device="cuda").view(torch.bfloat16)
+    vp = kp.clone()
+    pt = dev_i32(pc.page_table)
+    pkv.paged_kv_append(kp, vp, pt, dev_i32(pc.batch_idx), dev_i32(pc.input_pos), dev_bf16(pc.k),
+                        dev_bf16(pc.v), page_size=pc.page_size)
+    last = pc.cu_seqlens[1:] - 1
+    lens = pc.doc_lens().astype(np.int32)
+    slots = np.arange(1, pc.n_docs + 1, dtype=np.int32)
+    d_out, d_lse = pkv.paged_decode_attn(dev_bf16(pc.q[last]), kp, vp, pt, dev_i32(slots),
+                                         dev_i32(lens), page_size=pc.page_size,
+                                         scale=float(pc.scale), max_kv_len=int(lens.max()))
+    torch.cuda.synchronize()
+    check_close(d_out, d_lse, out_ref[last], lse_ref[last], "decode of last rows")
+    last_t = torch.from_numpy(last.astype(np.int64)).cuda()
+    check_close(d_out, d_lse, out.index_select(0, last_t).float().cpu().numpy().astype(np.float64),
+                lse.index_select(0, last_t).cpu().numpy().astype(np.float64),
+                "decode vs prefill (GPU both)")
