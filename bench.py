@@ -1,23 +1,28 @@
 """Benchmark of the paged-KV attention hot path on one MI355X.
 
 A step is one pass of the hot path over one batch of synthetic input:
-  decode: paged_kv_append of one new token per live sequence, then
-          paged_decode_attn over the bucketed B=64 batch (50 live rows,
-          14 padding rows in slot 0, contexts 512..1024, sequential pages,
-          H_q=32, H_kv=8, D=128, page_size=128);
+  decode:  paged_kv_append of one new token per live sequence, then
+           paged_decode_attn over the bucketed B=64 batch (50 live rows,
+           14 padding rows in slot 0, contexts 512..1024, sequential pages,
+           H_q=32, H_kv=8, D=128, page_size=128);
   prefill: paged_kv_append of the packed prompts' K/V into shuffled pages,
-          then packed_prefill_attn (64 prompts of 64..512 tokens, L ~ 18k).
-Every timed step starts after a cache-flush kernel reads 1 GiB (four times
-the 256 MiB Infinity Cache), so the KV bytes come from HBM.  Device time of each
-part is taken with HIP events on the stream the kernels run on and summed
-over the K timed steps; the flush is outside the events.
+           then packed_prefill_attn (64 prompts of 64..512 tokens, L ~ 18k).
 
-Prints one JSON line.  value = decode KV bytes per step / decode device time
+Cold data without a flush: like the layers of a model, the benchmark keeps
+several independent KV caches (and prefill inputs) and runs the steps back to
+back, rotating through them, so every call reads data that was last touched
+several calls (>1 GiB of other traffic) earlier and cannot still sit in the
+256 MiB Infinity Cache.  The K timed steps are bracketed by one pair of HIP
+events on the stream the kernels run on, after a synchronize on both sides.
+(--flush instead times each call alone after a 1 GiB read of another buffer.)
+
+Prints one JSON line.  value = decode KV bytes per step / decode step time
 (GB/s); the prefill part is reported under "prefill".
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -31,24 +36,61 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak, published
 METRIC = "paged decode KV-read GB/s (% of HBM peak) at B=64; prefill TFLOP/s"
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "paged_kv_attention_23_amd", "csrc")
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--layers", type=int, default=8,
+                    help="independent KV caches rotated through by the decode steps")
+    ap.add_argument("--prefill-layers", type=int, default=4,
+                    help="independent prefill input sets rotated through")
     ap.add_argument("--num-splits", type=int, default=0, help="decode split count (0 = auto)")
     ap.add_argument("--flags", type=int, default=0, help="decode PKV_F_* flags")
-    ap.add_argument("--no-flush", action="store_true", help="warm-cache timing (reported as such)")
+    ap.add_argument("--flush", action="store_true",
+                    help="time each call alone after a 1 GiB read of another buffer")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="budget for the CPU oracle baseline (0 = skip)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (counter calibration)")
     return ap.parse_args()
+
+
+def copy_probe(mib):
+    """A plain copy kernel of known size: the reference that scales the HBM byte counters."""
+    import torch
+
+    n = mib * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4}), flush=True)
+
+
+def measured_traffic(kernel: str, source: str):
+    """HBM bytes per launch from the committed counter runs, if the kernel is unchanged."""
+    try:
+        with open(TRAFFIC_JSON) as f:
+            t = json.load(f)[kernel]
+        with open(os.path.join(CSRC, source), "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, KeyError, ValueError):
+        return None
+    return int(t["traffic_bytes"]) if t.get("source_sha256") == sha else None
 
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path runs on a single MI355X)", file=sys.stderr)
@@ -57,7 +99,7 @@ def main():
     import torch
 
     import paged_kv_attention_23_amd as pkv
-    from workloads import make_case
+    from workloads import f32_to_bf16_bits, make_case
 
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from gpu_util import dev_bf16, dev_i32
@@ -67,16 +109,19 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
 
-    # ---------------- decode inputs (bucketed B=64)
+    # ---------------- decode inputs (bucketed B=64), one KV cache per layer
     c = make_case(3, fill="zero")
     rng = np.random.default_rng(9303)
     act = c.active_rows()
     app_bi = c.batch_idx[act].astype(np.int32)
     app_pos = (c.kv_len[act] - 1).astype(np.int32)         # the step's new token is key n-1
-    from workloads import f32_to_bf16_bits
     app_k = f32_to_bf16_bits(rng.standard_normal((len(act), c.H_kv, c.D), dtype=np.float32))
     app_v = f32_to_bf16_bits(rng.standard_normal((len(act), c.H_kv, c.D), dtype=np.float32))
-    d_q, d_k, d_v = dev_bf16(c.q), dev_bf16(c.k_pool), dev_bf16(c.v_pool)
+    d_q = dev_bf16(c.q)
+    k0, v0 = dev_bf16(c.k_pool), dev_bf16(c.v_pool)
+    NL = max(1, args.layers)
+    d_k = [k0] + [k0.clone() for _ in range(NL - 1)]
+    d_v = [v0] + [v0.clone() for _ in range(NL - 1)]
     d_pt, d_bi, d_kl = dev_i32(c.page_table), dev_i32(c.batch_idx), dev_i32(c.kv_len)
     d_abi, d_apos = dev_i32(app_bi), dev_i32(app_pos)
     d_ak, d_av = dev_bf16(app_k), dev_bf16(app_v)
@@ -88,101 +133,109 @@ def main():
     d_lse = torch.empty((c.B, c.H_q), dtype=torch.float32, device=dev)
     kv_bytes = c.kv_bytes()
 
-    def decode_step():
-        pkv.paged_kv_append(d_k, d_v, d_pt, d_abi, d_apos, d_ak, d_av, page_size=c.page_size)
-        pkv.paged_decode_attn(d_q, d_k, d_v, d_pt, d_bi, d_kl, page_size=c.page_size,
-                              scale=float(c.scale), max_kv_len=max_kv, num_splits=S,
-                              flags=args.flags, workspace=d_ws, out=d_out, lse=d_lse)
+    def decode_only(i):
+        pkv.paged_decode_attn(d_q, d_k[i % NL], d_v[i % NL], d_pt, d_bi, d_kl,
+                              page_size=c.page_size, scale=float(c.scale), max_kv_len=max_kv,
+                              num_splits=S, flags=args.flags, workspace=d_ws, out=d_out, lse=d_lse)
 
-    def decode_only():
-        pkv.paged_decode_attn(d_q, d_k, d_v, d_pt, d_bi, d_kl, page_size=c.page_size,
-                              scale=float(c.scale), max_kv_len=max_kv, num_splits=S,
-                              flags=args.flags, workspace=d_ws, out=d_out, lse=d_lse)
+    def decode_step(i):
+        pkv.paged_kv_append(d_k[i % NL], d_v[i % NL], d_pt, d_abi, d_apos, d_ak, d_av,
+                            page_size=c.page_size)
+        decode_only(i)
 
-    # Cache flush: read 1 GiB (4x the Infinity Cache) into a scalar.  A read
-    # leaves only clean lines behind, so the timed kernel does not pay for
-    # the flush's own write-backs.
-    flush_buf = torch.ones(1024 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
-    flush_sink = torch.empty((), dtype=torch.float32, device=dev)
-
-    def flush():
-        if not args.no_flush:
-            torch.sum(flush_buf, dim=0, out=flush_sink)
-
-    def timed(fn, n):
-        """Sum of device times of n calls of fn, each after a flush."""
-        total = 0.0
-        times = []
-        for _ in range(n):
-            flush()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-            e1.synchronize()
-            ms = e0.elapsed_time(e1)
-            times.append(ms)
-            total += ms
-        return total, times
-
-    # ---------------- prefill inputs (packed 64 prompts)
+    # ---------------- prefill inputs (packed 64 prompts), one input set per layer
     prefill = None
     if not args.no_prefill:
         pc = make_case(5)
-        p_q, p_k, p_v = dev_bf16(pc.q), dev_bf16(pc.k), dev_bf16(pc.v)
+        NP = max(1, args.prefill_layers)
+        p_q = [dev_bf16(pc.q)]
+        p_k = [dev_bf16(pc.k)]
+        p_v = [dev_bf16(pc.v)]
+        for _ in range(NP - 1):
+            p_q.append(p_q[0].clone())
+            p_k.append(p_k[0].clone())
+            p_v.append(p_v[0].clone())
         p_cu = dev_i32(pc.cu_seqlens)
         p_pt, p_bi, p_ip = dev_i32(pc.page_table), dev_i32(pc.batch_idx), dev_i32(pc.input_pos)
-        p_kpool = torch.zeros((pc.H_kv, pc.num_pages * pc.page_size, pc.D), dtype=torch.bfloat16,
-                              device=dev)
-        p_vpool = torch.zeros_like(p_kpool)
+        shape = (pc.H_kv, pc.num_pages * pc.page_size, pc.D)
+        p_kpool = [torch.zeros(shape, dtype=torch.bfloat16, device=dev) for _ in range(NP)]
+        p_vpool = [torch.zeros(shape, dtype=torch.bfloat16, device=dev) for _ in range(NP)]
         p_out = torch.empty((pc.L, pc.H_q, pc.D), dtype=torch.bfloat16, device=dev)
         p_lse = torch.empty((pc.L, pc.H_q), dtype=torch.float32, device=dev)
 
-        def prefill_attn():
-            pkv.packed_prefill_attn(p_q, p_k, p_v, p_cu, scale=float(pc.scale), out=p_out, lse=p_lse)
+        def prefill_attn(i):
+            j = i % NP
+            pkv.packed_prefill_attn(p_q[j], p_k[j], p_v[j], p_cu, scale=float(pc.scale),
+                                    out=p_out, lse=p_lse)
 
-        def prefill_step():
-            pkv.paged_kv_append(p_kpool, p_vpool, p_pt, p_bi, p_ip, p_k, p_v, page_size=pc.page_size)
-            prefill_attn()
+        def prefill_step(i):
+            j = i % NP
+            pkv.paged_kv_append(p_kpool[j], p_vpool[j], p_pt, p_bi, p_ip, p_k[j], p_v[j],
+                                page_size=pc.page_size)
+            prefill_attn(i)
 
-        try:
-            prefill_step()
-            torch.cuda.synchronize()
-            prefill = dict(case=pc, step=prefill_step, attn=prefill_attn)
-        except RuntimeError as e:  # kernel not available in this build
-            print(f"prefill skipped: {e}", file=sys.stderr)
+        prefill = dict(case=pc, step=prefill_step, attn=prefill_attn, layers=NP)
+
+    flush_buf = torch.ones(1024 * 1024 * 1024 // 4, dtype=torch.float32, device=dev) \
+        if args.flush else None
+    flush_sink = torch.empty((), dtype=torch.float32, device=dev)
+
+    def timed(fn, n):
+        """Device time (ms) of n steps fn(0..n-1)."""
+        if args.flush:  # each call alone after a 1 GiB read (clean eviction)
+            total = 0.0
+            for i in range(n):
+                torch.sum(flush_buf, dim=0, out=flush_sink)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn(i)
+                e1.record(stream)
+                e1.synchronize()
+                total += e0.elapsed_time(e1)
+            return total
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1)
 
     # ---------------- warmup
-    for _ in range(args.warmup):
-        decode_step()
+    for i in range(args.warmup):
+        decode_step(i)
         if prefill:
-            prefill["step"]()
+            prefill["step"](i)
     torch.cuda.synchronize()
 
     # ---------------- timed steps
-    torch.cuda.synchronize()
+    K = args.steps
     t0 = time.perf_counter()
-    dec_total, dec_times = timed(decode_step, args.steps)
-    pre_total, pre_times = (timed(prefill["step"], args.steps) if prefill else (0.0, []))
+    dec_total = timed(decode_step, K)
+    pre_total = timed(prefill["step"], K) if prefill else 0.0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # decode kernel alone (the dominant kernel for the roofline) and the attention part of prefill
-    dk_total, dk_times = timed(decode_only, args.steps)
-    pa_total, pa_times = (timed(prefill["attn"], args.steps) if prefill else (0.0, []))
+    # the dominant kernels alone (roofline): decode attention, prefill attention
+    dk_total = timed(decode_only, K)
+    pa_total = timed(prefill["attn"], K) if prefill else 0.0
 
-    dec_ms = dec_total / args.steps
-    dk_ms = dk_total / args.steps
+    dec_ms, dk_ms = dec_total / K, dk_total / K
     value = kv_bytes / (dec_ms * 1e-3) / 1e9
     achieved = kv_bytes / (dk_ms * 1e-3) / 1e9
+    cache = ("flushed: 1 GiB read before each call" if args.flush else
+             f"cold: {NL} KV caches (one per layer) read round-robin, "
+             f"{(NL - 1) * kv_bytes / 1e9:.2f} GB of other KV between reuses")
     out = {
         "metric": METRIC,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": K,
         "warmup": args.warmup,
-        "ms_per_step": round((dec_total + pre_total) / args.steps, 5),
+        "ms_per_step": round((dec_total + pre_total) / K, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -194,21 +247,20 @@ def main():
                         "sequential pages, + append of 1 token per live row",
             "global_batch": int(c.B),
             "kv_bytes_per_step": int(kv_bytes),
+            "decode_step_ms": round(dec_ms, 5),
             "num_splits": int(S),
             "flags": int(args.flags),
-            "cache": "warm" if args.no_flush else "flushed (1 GiB read before each step)",
-            "decode_step_ms_median": round(float(np.median(dec_times)), 5),
-            "decode_step_ms_best": round(float(np.min(dec_times)), 5),
+            "cache": cache,
             "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_decode_attn (decode_kernel%s)" % (" + merge_kernel" if S > 1 else ""),
+            "kernel": "decode_kernel%s (paged_decode_attn)" % (" + merge_kernel" if S > 1 else ""),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic("decode_kernel", "decode.hip"),
             "avg_call_us": round(dk_ms * 1e3, 3),
             "algorithmic_bytes_per_call": int(kv_bytes),
         },
@@ -217,16 +269,25 @@ def main():
     if prefill:
         pc = prefill["case"]
         flops = pc.flops()
-        pa_ms = pa_total / args.steps
-        pre_ms = pre_total / args.steps
+        pa_ms, pre_ms = pa_total / K, pre_total / K
+        tflops = flops / (pa_ms * 1e-3) / 1e12
         out["prefill"] = {
             "workload": "packed prefill, 64 prompts U[64,512] (L=%d), H_q=32 H_kv=8 D=128, "
                         "document-causal, + append into shuffled 128-token pages" % pc.L,
             "flops_per_call": int(flops),
-            "attn_ms": round(pa_ms, 5),
-            "step_ms": round(pre_ms, 5),
-            "tflops": round(flops / (pa_ms * 1e-3) / 1e12, 2),
-            "frac_of_bf16_peak": round(flops / (pa_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "attn_us": round(pa_ms * 1e3, 3),
+            "step_us": round(pre_ms * 1e3, 3),
+            "tflops": round(tflops, 2),
+            "roofline": {
+                "bound": "mfma",
+                "kernel": "prefill_kernel (packed_prefill_attn)",
+                "achieved": round(tflops, 2),
+                "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s",
+                "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic("prefill_kernel", "prefill.hip"),
+            },
+            "cache": f"cold: {prefill['layers']} input sets read round-robin",
         }
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(c, kv_bytes, args.cpu_seconds)
@@ -251,8 +312,8 @@ def cpu_baseline(c, kv_bytes, budget_s):
         "unit": "GB/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": f"the full B=64 decode step (50 live rows), repeated {reps}x "
-                  f"in {t_total:.1f} s",
+        "sample": f"the full B=64 decode step (50 live rows, {kv_bytes / 1e6:.1f} MB of KV), "
+                  f"repeated {reps}x in {t_total:.1f} s",
     }
 
 
