@@ -123,7 +123,7 @@ int32_t paged_decode_num_splits(int32_t batch, int32_t num_kv_heads, int32_t max
  * Results are bitwise reproducible for identical inputs and split count.
  * batch == 0 is a valid no-op.  Requirements: head_dim 64 or 128,
  * num_q_heads a multiple of num_kv_heads with at most 16 query heads per
- * KV head, page_size a power of two >= 16.
+ * KV head, page_size a power of two >= 16, scale finite and > 0.
  */
 int paged_decode_attn(const void *q, const void *k_pool, const void *v_pool, int32_t num_pages,
                       int32_t page_size, int32_t num_kv_heads, int32_t head_dim,
@@ -151,7 +151,8 @@ int paged_decode_attn(const void *q, const void *k_pool, const void *v_pool, int
  *   lse          fp32 [total_len][num_q_heads] (natural log)
  *
  * total_len == 0 is a valid no-op.  Requirements: head_dim 128, num_q_heads a
- * multiple of num_kv_heads.
+ * multiple of num_kv_heads with at most 16 query heads per KV head, scale
+ * finite and > 0.
  */
 int packed_prefill_attn(const void *q, const void *k, const void *v, const int32_t *cu_seqlens,
                         int32_t num_docs, int32_t total_len, int32_t num_q_heads,

@@ -165,8 +165,8 @@ __device__ __forceinline__ void compute_tile(const u32x4 (&k)[2][D / 32], int kt
   float mt = x[0];
 #pragma unroll
   for (int i = 1; i < 8; ++i) mt = fmaxf(mt, x[i]);
-  mt = fmaxf(mt, shfl_xor_f(mt, 16));
-  mt = fmaxf(mt, shfl_xor_f(mt, 32));
+  mt = max_xor16(mt);
+  mt = max_xor32(mt);
   const float m_new = fmaxf(m_run, mt);
   const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
   const float alpha = fast_exp2(m_run - m_use);
@@ -216,7 +216,7 @@ __device__ __forceinline__ void compute_tile(const u32x4 (&k)[2][D / 32], int kt
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t a0 = rv[2 * j][t >> 1], a1 = rv[2 * j + 1][t >> 1];
-      w[j] = (t & 1) ? ((a0 >> 16) | (a1 & 0xffff0000u)) : ((a0 & 0xffffu) | (a1 << 16));
+      w[j] = pair_halves(a0, a1, t & 1);
     }
     const u32x4 vw = {w[0], w[1], w[2], w[3]};
     o[t] = mfma16x16x32(as_bf16x8(vw), pop, o[t]);
@@ -274,9 +274,11 @@ void decode_kernel(DecodeArgs a) {
   int n = a.kv_len[r];
   n = min(n, a.max_blocks << a.page_shift);
   const bool pad = (s <= 0) || (s >= a.num_slots) || (n <= 0);
-  const int64_t lo64 = (int64_t)sp * a.chunk;
+  // Split sp covers an equal share of this row's keys, in whole 32-key tiles.
+  const int chunk = ((n + a.num_splits - 1) / a.num_splits + kTileKeys - 1) & ~(kTileKeys - 1);
+  const int64_t lo64 = (int64_t)sp * chunk;
   const int lo = (int)min(lo64, (int64_t)n);
-  const int hi = (sp == a.num_splits - 1) ? n : (int)min((int64_t)n, lo64 + a.chunk);
+  const int hi = (sp == a.num_splits - 1) ? n : (int)min((int64_t)n, lo64 + chunk);
   if (pad || lo >= hi) {
     write_empty(a, r, g, sp);
     return;
@@ -354,8 +356,8 @@ void decode_kernel(DecodeArgs a) {
   }
 
   // Combine the 4 waves through LDS (the merge area reuses the V tiles).
-  l_run += shfl_xor_f(l_run, 16);
-  l_run += shfl_xor_f(l_run, 32);
+  l_run = sum_xor16(l_run);
+  l_run = sum_xor32(l_run);
   __syncthreads();
   float *mo = reinterpret_cast<float *>(smem);        // [wave][16 heads][D]
   float *mm = mo + kDecWaves * 16 * D;                // [wave][16]

@@ -73,7 +73,6 @@ int device_cus() {
   return cus;
 }
 
-constexpr int kTileKeys = 32;
 constexpr int kMinSplitKeys = 256;
 
 int32_t auto_splits(int32_t batch, int32_t num_kv_heads, int32_t max_kv_len, int cus) {
@@ -159,7 +158,7 @@ int paged_decode_attn(const void *q, const void *k_pool, const void *v_pool, int
   if (num_q_heads / num_kv_heads > 16)
     return fail(PKV_E_SHAPE, "at most 16 query heads per KV head are supported (got %d)",
                 num_q_heads / num_kv_heads);
-  if (!(scale == scale) || isinf(scale)) return fail(PKV_E_SHAPE, "scale must be finite");
+  if (!(scale > 0.f) || isinf(scale)) return fail(PKV_E_SHAPE, "scale must be finite and positive");
   if (num_splits < 0 || num_splits > PKV_MAX_SPLITS)
     return fail(PKV_E_SPLITS, "num_splits must be in [0, %d] (got %d)", PKV_MAX_SPLITS, num_splits);
   if (flags & ~(uint32_t)(PKV_F_ASSUME_CONTIGUOUS | PKV_F_NO_CONTIG_DETECT))
@@ -178,9 +177,6 @@ int paged_decode_attn(const void *q, const void *k_pool, const void *v_pool, int
   const int32_t kv_bound = (max_kv_len <= 0 || max_kv_len > cap) ? cap : max_kv_len;
   int32_t S = num_splits;
   if (S == 0) S = auto_splits(batch, num_kv_heads, kv_bound, device_cus());
-  int32_t chunk = (kv_bound + S - 1) / S;
-  chunk = (chunk + kTileKeys - 1) / kTileKeys * kTileKeys;
-  if (chunk <= 0) chunk = kTileKeys;
 
   pkv::DecodeArgs a;
   a.o_part = nullptr;
@@ -214,7 +210,6 @@ int paged_decode_attn(const void *q, const void *k_pool, const void *v_pool, int
   a.D = head_dim;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.num_splits = S;
-  a.chunk = chunk;
   a.contig_mode = (flags & PKV_F_NO_CONTIG_DETECT) ? 2 : (flags & PKV_F_ASSUME_CONTIGUOUS) ? 1 : 0;
   a.out = (uint16_t *)out;
   a.lse = lse;
@@ -234,7 +229,7 @@ int packed_prefill_attn(const void *q, const void *k, const void *v, const int32
   if (num_q_heads / num_kv_heads > 16)
     return fail(PKV_E_SHAPE, "at most 16 query heads per KV head are supported (got %d)",
                 num_q_heads / num_kv_heads);
-  if (!(scale == scale) || isinf(scale)) return fail(PKV_E_SHAPE, "scale must be finite");
+  if (!(scale > 0.f) || isinf(scale)) return fail(PKV_E_SHAPE, "scale must be finite and positive");
   if (total_len == 0) return PKV_OK;
   if (num_docs == 0) return fail(PKV_E_SHAPE, "total_len > 0 needs at least one document");
   if (!q || !k || !v || !cu_seqlens || !out || !lse)

@@ -40,6 +40,35 @@ __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
   return __shfl_xor(v, mask, kWave);
 }
 
+// Cross-row butterfly steps on the gfx950 lane-swap instructions.  Swapping a
+// register with itself returns, per lane, the pair {own value, value of lane
+// l ^ 16} (permlane16_swap) or {own, lane l ^ 32} (permlane32_swap) in some
+// order, so a symmetric combine of the pair is the xor-16 / xor-32 step.
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Pair the low (hi = false) or high (hi = true) bf16 halves of two words:
+// result = {a0.half, a1.half} (a0's half in the low 16 bits), one v_perm_b32.
+// v_perm_b32 selector bytes 0-3 pick bytes of its second source, 4-7 bytes of
+// its first source.
+__device__ __forceinline__ uint32_t pair_halves(uint32_t a0, uint32_t a1, bool hi) {
+  return __builtin_amdgcn_perm(a1, a0, hi ? 0x07060302u : 0x05040100u);
+}
 
 }  // namespace pkv

@@ -25,7 +25,7 @@ struct DecodeArgs {
   int32_t num_pages, page_shift, num_slots, max_blocks;
   int32_t B, H_q, H_kv, G, D;
   float scale_log2;                // scale * log2(e)
-  int32_t num_splits, chunk;       // keys per split (multiple of the 32-key tile)
+  int32_t num_splits;              // key splits per row (each gets an equal share)
   int32_t contig_mode;             // 0 detect per row, 1 assume contiguous, 2 never
   float *o_part, *lse_part;        // split partials [S][B][H_q][D], [S][B][H_q]
   uint16_t *out;                   // [B][H_q][D] bf16

@@ -40,6 +40,7 @@ constexpr int kPfRowStride = 2 * kPfD + 16;          // bytes per key row in LDS
 constexpr int kPfTileBytes = kPfBN * kPfRowStride;   // one K or V stage
 constexpr int kPfSmem = 2 * 2 * kPfTileBytes;        // 2 stages x (K, V)
 constexpr int kPfLoads = kPfBN * (2 * kPfD / 16) / kPfThreads;  // 16-byte pieces per thread per tensor
+constexpr float kLazy = 8.f;                         // lazy-rescale threshold, log2 units
 
 struct PfTile {
   int doc_start, q_lo, q_hi;
@@ -48,27 +49,51 @@ struct PfTile {
 // Tile number -> (document, query tile), longest key range first: level j
 // holds query tile j of every document with more than j tiles, levels in
 // descending j, documents in order within a level.  Every wave computes this
-// redundantly from cu_seqlens (a few loads that hit in cache).
-__device__ bool find_tile(const int32_t *cu, int num_docs, int QT, int tile, int lane, PfTile &out) {
-  // longest document, in tiles
+// redundantly.  Tile counts of up to 256 documents are loaded once into
+// registers (lane d of chunk c holds document 64*c + d), so each level is a
+// few ballots; longer document lists reload per level.
+__device__ __forceinline__ int ceil_div_qt(int x, int QT, int qt_shift) {
+  return qt_shift >= 0 ? (x + QT - 1) >> qt_shift : (x + QT - 1) / QT;
+}
+
+__device__ bool find_tile(const int32_t *cu, int num_docs, int QT, int qt_shift, int tile, int lane,
+                          PfTile &out) {
+  constexpr int kCached = 4;  // 64-document chunks held in registers
+  int tcount[kCached];
   int jmax = 0;
+#pragma unroll
+  for (int c = 0; c < kCached; ++c) {
+    const int d = 64 * c + lane;
+    tcount[c] = (d < num_docs) ? ceil_div_qt(cu[d + 1] - cu[d], QT, qt_shift) : 0;
+  }
   for (int d0 = 0; d0 < num_docs; d0 += kWave) {
     const int d = d0 + lane;
     int t = 0;
-    if (d < num_docs) t = (cu[d + 1] - cu[d] + QT - 1) / QT;
+    if (d0 < kCached * kWave) {
+#pragma unroll
+      for (int c = 0; c < kCached; ++c)
+        if (d0 == 64 * c) t = tcount[c];
+    } else if (d < num_docs) {
+      t = ceil_div_qt(cu[d + 1] - cu[d], QT, qt_shift);
+    }
     for (int m = 1; m < kWave; m <<= 1) t = max(t, __shfl_xor(t, m, kWave));
     jmax = max(jmax, t);
   }
   for (int j = jmax - 1; j >= 0; --j) {
     for (int d0 = 0; d0 < num_docs; d0 += kWave) {
       const int d = d0 + lane;
-      bool has = false;
-      if (d < num_docs) has = (cu[d + 1] - cu[d]) > j * QT;
-      const uint64_t mask = __ballot(has);
+      int t = 0;
+      if (d0 < kCached * kWave) {
+#pragma unroll
+        for (int c = 0; c < kCached; ++c)
+          if (d0 == 64 * c) t = tcount[c];
+      } else if (d < num_docs) {
+        t = ceil_div_qt(cu[d + 1] - cu[d], QT, qt_shift);
+      }
+      const uint64_t mask = __ballot(t > j);
       const int cnt = __popcll(mask);
       if (tile < cnt) {
-        // position of the tile-th set bit
-        uint64_t m = mask;
+        uint64_t m = mask;  // position of the tile-th set bit
         for (int k = 0; k < tile; ++k) m &= m - 1;
         const int dd = d0 + __builtin_ctzll(m);
         out.doc_start = cu[dd];
@@ -93,9 +118,10 @@ void prefill_kernel(PrefillArgs a) {
   const int tile = blockIdx.x / a.H_kv;
   const int G = a.G;
   const int QT = kPfRows / G;  // query rows per tile
+  const int qt_shift = (QT & (QT - 1)) == 0 ? __builtin_ctz(QT) : -1;
 
   PfTile tl;
-  if (!find_tile(a.cu_seqlens, a.num_docs, QT, tile, lane, tl)) return;  // uniform
+  if (!find_tile(a.cu_seqlens, a.num_docs, QT, qt_shift, tile, lane, tl)) return;  // uniform
   const int k_lo = tl.doc_start, k_hi = tl.q_hi;
 
   // Rows of this wave: column block qb, column hl -> tile row R.
@@ -105,7 +131,8 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int R = 32 * wave + 16 * qb + hl;
-    const int hh = R / QT, qq = tl.q_lo + R % QT;
+    const int hh = qt_shift >= 0 ? R >> qt_shift : R / QT;
+    const int qq = tl.q_lo + (qt_shift >= 0 ? R & (QT - 1) : R % QT);
     col_ok[qb] = (hh < G) && (qq < tl.q_hi);
     col_head[qb] = g * G + min(hh, G - 1);
     col_q[qb] = col_ok[qb] ? qq : k_lo - 1;  // unused columns mask every key
@@ -163,12 +190,8 @@ void prefill_kernel(PrefillArgs a) {
     if (s + 1 < nsteps) load_stage(s + 1);
     const char *kb = smem + buf * 2 * kPfTileBytes;
     const char *vb = kb + kPfTileBytes;
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {  // two 32-key halves of the stage
-      const int key0 = k_lo + s * kPfBN + 32 * h2;
-      if (key0 >= k_hi) break;  // uniform
-      // S^T blocks: keys key0 + 16*kb2 + (4*lg + i), columns qb.
-      f32x4 sc[2][2];
+    // S^T blocks of a 32-key half: keys key0 + 16*kb2 + (4*lg + i), columns qb.
+    auto qk = [&](int h2, f32x4 (&sc)[2][2]) {
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
         bf16x8 kop[D / 32];
@@ -183,45 +206,10 @@ void prefill_kernel(PrefillArgs a) {
           sc[kb2][qb] = acc;
         }
       }
+    };
+    auto softmax_pv = [&](int h2, const f32x4 (&sc)[2][2]) {
+      const int key0 = k_lo + s * kPfBN + 32 * h2;
       const bool diag = key0 + 31 >= q_first;  // some key may lie past some query row
-      bf16x8 pop[2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        float x[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[i] = sc[0][qb][i] * a.scale_log2;
-          x[4 + i] = sc[1][qb][i] * a.scale_log2;
-        }
-        if (diag) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int key = key0 + (i < 4 ? 4 * lg + i : 16 + 4 * lg + (i - 4));
-            if (key > col_q[qb]) x[i] = -INFINITY;
-          }
-        }
-        float mt = x[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) mt = fmaxf(mt, x[i]);
-        mt = fmaxf(mt, shfl_xor_f(mt, 16));
-        mt = fmaxf(mt, shfl_xor_f(mt, 32));
-        const float m_new = fmaxf(m_run[qb], mt);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run[qb] - m_use);
-        float p[8], ps = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          p[i] = fast_exp2(x[i] - m_use);
-          ps += p[i];
-        }
-        l_run[qb] = l_run[qb] * alpha + ps;
-        m_run[qb] = m_new;
-#pragma unroll
-        for (int t = 0; t < D / 16; ++t) o[qb][t] *= alpha;
-        const u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                          pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-        pop[qb] = as_bf16x8(pw);
-      }
       // V^T operands: lane reads V[key kappa(lg, e)][8*hl .. 8*hl+7]; step t
       // uses head_dim d = 8*m + t for its row m.
       uint32_t rv[8][4];
@@ -232,18 +220,71 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) rv[e][j] = w[j];
       }
+      bf16x8 pop[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        // raw scores; scale (> 0) is applied to the max and inside the exponent
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[i] = sc[0][qb][i];
+          x[4 + i] = sc[1][qb][i];
+        }
+        if (diag) {
+          const int lim = col_q[qb] - key0 - 4 * lg;  // key offset i is live iff i <= lim
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int off = i < 4 ? i : 16 + (i - 4);
+            if (off > lim) x[i] = -INFINITY;
+          }
+        }
+        float mt = x[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) mt = fmaxf(mt, x[i]);
+        mt = max_xor16(mt);
+        mt = max_xor32(mt);
+        mt *= a.scale_log2;
+        // Lazy rescaling: the reference point m_run only moves when some
+        // lane's tile max exceeds it by more than kLazy (log2 units); until
+        // then p <= 2^kLazy and no accumulator needs rescaling.
+        if (__any(mt > m_run[qb] + kLazy)) {
+          const float m_new = fmaxf(m_run[qb], mt);
+          if (__any(m_run[qb] != -INFINITY)) {  // otherwise o and l are still zero
+            const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run[qb] - m_new);
+            l_run[qb] *= alpha;
+#pragma unroll
+            for (int t = 0; t < D / 16; ++t) o[qb][t] *= alpha;
+          }
+          m_run[qb] = m_new;
+        }
+        const float m_use = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
+        float p[8], ps = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          p[i] = fast_exp2(fmaf(x[i], a.scale_log2, -m_use));
+          ps += p[i];
+        }
+        l_run[qb] += ps;
+        const u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                          pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+        pop[qb] = as_bf16x8(pw);
+      }
 #pragma unroll
       for (int t = 0; t < D / 16; ++t) {
         uint32_t w[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t a0 = rv[2 * j][t >> 1], a1 = rv[2 * j + 1][t >> 1];
-          w[j] = (t & 1) ? ((a0 >> 16) | (a1 & 0xffff0000u)) : ((a0 & 0xffffu) | (a1 << 16));
-        }
+        for (int j = 0; j < 4; ++j) w[j] = pair_halves(rv[2 * j][t >> 1], rv[2 * j + 1][t >> 1], t & 1);
         const bf16x8 vop = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) o[qb][t] = mfma16x16x32(vop, pop[qb], o[qb][t]);
       }
+    };
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {  // two 32-key halves of the stage
+      if (k_lo + s * kPfBN + 32 * h2 >= k_hi) break;  // uniform
+      f32x4 sc[2][2];
+      qk(h2, sc);
+      softmax_pv(h2, sc);
     }
     if (s + 1 < nsteps) store_stage(s + 1, buf ^ 1);
     __syncthreads();
@@ -253,8 +294,8 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     float l = l_run[qb];
-    l += shfl_xor_f(l, 16);
-    l += shfl_xor_f(l, 32);
+    l = sum_xor16(l);
+    l = sum_xor32(l);
     if (!col_ok[qb]) continue;
     const float inv = (l > 0.f) ? 1.f / l : 0.f;
     const int64_t rh = (int64_t)col_q[qb] * a.H_q + col_head[qb];

@@ -69,6 +69,8 @@ def _decode(lib, **kw):
     (dict(num_pages=0), -2, "num_pages"),
     (dict(max_blocks=0), -2, "max_blocks"),
     (dict(scale=float("nan")), -2, "scale"),
+    (dict(scale=-0.125), -2, "scale"),
+    (dict(scale=0.0), -2, "scale"),
     (dict(splits=65), -5, "num_splits"),
     (dict(splits=-1), -5, "num_splits"),
     (dict(flags=8), -2, "flag"),
