@@ -12,9 +12,12 @@ Cold data without a flush: like the layers of a model, the benchmark keeps
 several independent KV caches (and prefill inputs) and runs the steps back to
 back, rotating through them, so every call reads data that was last touched
 several calls (>1 GiB of other traffic) earlier and cannot still sit in the
-256 MiB Infinity Cache.  The K timed steps are bracketed by one pair of HIP
-events on the stream the kernels run on, after a synchronize on both sides.
-(--flush instead times each call alone after a 1 GiB read of another buffer.)
+256 MiB Infinity Cache.  The K timed steps are captured into one HIP graph
+(as a serving loop captures its decode step per batch bucket, the pages'
+CUDA-graph setup) and replayed once, bracketed by one pair of HIP events on
+the stream they run on, after a synchronize on both sides; --eager launches
+each call from Python instead.  (--flush times each call alone after a 1 GiB
+read of another buffer.)
 
 Prints one JSON line.  value = decode KV bytes per step / decode step time
 (GB/s); the prefill part is reported under "prefill".
@@ -49,8 +52,12 @@ def parse():
                     help="independent KV caches rotated through by the decode steps")
     ap.add_argument("--prefill-layers", type=int, default=4,
                     help="independent prefill input sets rotated through")
-    ap.add_argument("--num-splits", type=int, default=0, help="decode split count (0 = auto)")
-    ap.add_argument("--flags", type=int, default=0, help="decode PKV_F_* flags")
+    ap.add_argument("--num-splits", type=int, default=0,
+                    help="decode split count: 0 = automatic, 1 = single pass, >1 = per-row splits")
+    ap.add_argument("--flags", type=int, default=0,
+                    help="decode PKV_F_* flags (4 = balanced schedule, with --num-splits 0)")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every timed call from Python instead of replaying a HIP graph")
     ap.add_argument("--flush", action="store_true",
                     help="time each call alone after a 1 GiB read of another buffer")
     ap.add_argument("--no-prefill", action="store_true")
@@ -72,6 +79,15 @@ def copy_probe(mib):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4}), flush=True)
+
+
+def decode_kernels(S: int, W: int) -> str:
+    """The kernels one paged_decode_attn call launches for this schedule."""
+    if W > 1:
+        return "decode_balanced_kernel + merge_balanced_kernel"
+    if S > 1:
+        return "decode_rows_kernel + merge_rows_kernel"
+    return "decode_rows_kernel"
 
 
 def measured_traffic(kernel: str, source: str):
@@ -126,8 +142,10 @@ def main():
     d_abi, d_apos = dev_i32(app_bi), dev_i32(app_pos)
     d_ak, d_av = dev_bf16(app_k), dev_bf16(app_v)
     max_kv = int(c.kv_len.max())
-    S = args.num_splits or pkv.paged_decode_num_splits(c.B, c.H_kv, max_kv)
-    ws_bytes = pkv.paged_decode_workspace_size(c.B, c.H_q, c.D, S)
+    balanced = bool(args.flags & pkv.PKV_F_BALANCED)
+    S = args.num_splits or (0 if balanced else pkv.paged_decode_num_splits(c.B, c.H_kv, max_kv))
+    W = pkv.paged_decode_balanced_parts(c.B, c.H_kv, max_kv) if balanced else 0
+    ws_bytes = pkv.paged_decode_workspace_size(c.B, c.H_q, c.H_kv, c.D, S, args.flags)
     d_ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     d_out = torch.empty((c.B, c.H_q, c.D), dtype=torch.bfloat16, device=dev)
     d_lse = torch.empty((c.B, c.H_q), dtype=torch.float32, device=dev)
@@ -194,12 +212,30 @@ def main():
                 e1.synchronize()
                 total += e0.elapsed_time(e1)
             return total
+        if args.eager:
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(n):
+                fn(i)
+            e1.record(stream)
+            e1.synchronize()
+            return e0.elapsed_time(e1)
+        # The n steps are captured once into a HIP graph (as a serving loop
+        # captures its decode step) and replayed: the timed region holds the
+        # GPU work only, not Python's per-call launch cost.  All buffers are
+        # allocated before the capture; no memset is recorded.
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(n):
+                fn(i)
+        graph.replay()                      # first replay uploads the graph
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for i in range(n):
-            fn(i)
+        graph.replay()
         e1.record(stream)
         e1.synchronize()
         return e0.elapsed_time(e1)
@@ -248,19 +284,22 @@ def main():
             "global_batch": int(c.B),
             "kv_bytes_per_step": int(kv_bytes),
             "decode_step_ms": round(dec_ms, 5),
-            "num_splits": int(S),
+            "schedule": (f"balanced: {W} workgroups per KV head" if balanced else
+                         f"per-row: {S} split(s) per row"),
+            "launch": "eager stream launches" if (args.eager or args.flush) else
+                      f"one HIP graph of the {K} timed steps, replayed once",
             "flags": int(args.flags),
             "cache": cache,
             "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_kernel%s (paged_decode_attn)" % (" + merge_kernel" if S > 1 else ""),
+            "kernel": decode_kernels(S, W) + " (one paged_decode_attn call)",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic("decode_kernel", "decode.hip"),
+            "traffic": measured_traffic("decode", "decode.hip"),
             "avg_call_us": round(dk_ms * 1e3, 3),
             "algorithmic_bytes_per_call": int(kv_bytes),
         },
@@ -285,7 +324,7 @@ def main():
                 "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s",
                 "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
-                "traffic": measured_traffic("prefill_kernel", "prefill.hip"),
+                "traffic": measured_traffic("prefill", "prefill.hip"),
             },
             "cache": f"cold: {prefill['layers']} input sets read round-robin",
         }

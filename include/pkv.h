@@ -44,6 +44,7 @@ extern "C" {
 /* paged_decode_attn flags */
 #define PKV_F_ASSUME_CONTIGUOUS (1u << 0) /* caller promises each row's pages are consecutive ids */
 #define PKV_F_NO_CONTIG_DETECT (1u << 1)  /* always walk the page table block by block */
+#define PKV_F_BALANCED (1u << 2)          /* balanced split points across rows (num_splits = 0) */
 
 #define PKV_MAX_SPLITS 64
 
@@ -77,16 +78,30 @@ int paged_kv_append(void *k_pool, void *v_pool, int32_t num_pages, int32_t page_
 
 /*
  * paged_decode_workspace_size - bytes of workspace paged_decode_attn needs
- * for `num_splits` key splits (0 for num_splits <= 1).  Pure host function.
+ * for these num_splits and flags (the same values as in the call).  For
+ * num_splits == 0 without PKV_F_BALANCED it covers the largest split count
+ * the automatic choice can make for this batch; with PKV_F_BALANCED it
+ * depends on the shape and the current device's compute-unit count, not on
+ * the batch or the context lengths.  0 when no workspace is needed or for
+ * invalid shapes.  Host function.
  */
-size_t paged_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t head_dim,
-                                   int32_t num_splits);
+size_t paged_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t num_splits, uint32_t flags);
 
 /*
- * paged_decode_num_splits - the split count paged_decode_attn chooses when
- * called with num_splits = 0 on the current device.  Host function.
+ * paged_decode_num_splits - the per-row split count paged_decode_attn
+ * chooses for num_splits == 0 (without PKV_F_BALANCED) on the current device.
+ * Host function.
  */
 int32_t paged_decode_num_splits(int32_t batch, int32_t num_kv_heads, int32_t max_kv_len);
+
+/*
+ * paged_decode_balanced_parts - the number W of workgroups per KV head that
+ * the balanced schedule (PKV_F_BALANCED) uses on the current device for this
+ * batch and max_kv_len; W == 1 means a single pass with no merge.  Host
+ * function.
+ */
+int32_t paged_decode_balanced_parts(int32_t batch, int32_t num_kv_heads, int32_t max_kv_len);
 
 /*
  * paged_decode_attn - one query token per row attends to its row's cached keys.
@@ -109,18 +124,33 @@ int32_t paged_decode_num_splits(int32_t batch, int32_t num_kv_heads, int32_t max
  *   page_table   int32 [num_slots][max_blocks]
  *   batch_idx    int32 [batch]
  *   kv_len       int32 [batch]; values above max_blocks*page_size are clamped
- *   max_kv_len   host upper bound of kv_len used to plan key splits (<= 0 or
- *                above max_blocks*page_size means max_blocks*page_size); a
+ *   max_kv_len   host upper bound of kv_len used to plan the key splits (<= 0
+ *                or above max_blocks*page_size means max_blocks*page_size); a
  *                loose bound costs speed, never correctness
- *   num_splits   0 = choose automatically, 1 = single pass, 2..PKV_MAX_SPLITS
- *                = split-K partials plus a log-sum-exp merge kernel
- *   flags        PKV_F_* above
- *   workspace    device buffer of paged_decode_workspace_size(...) bytes for the
- *                chosen split count (may be NULL when that size is 0)
+ *   num_splits   split-K (flash-decoding; the pages leave the decode kernel's
+ *                work split open, so the schedules are the library's own):
+ *                0 = automatic per-row split count (paged_decode_num_splits),
+ *                1 = one workgroup per (row, KV head), single pass,
+ *                2..PKV_MAX_SPLITS = each row's keys in that many equal parts,
+ *                    merged by log-sum-exp in a second kernel.
+ *                Must be 0 with PKV_F_BALANCED.
+ *   flags        PKV_F_* above.  PKV_F_BALANCED selects the balanced schedule:
+ *                for each KV head the 32-key tiles of all rows, row after row,
+ *                are dealt in equal contiguous shares to W workgroups
+ *                (paged_decode_balanced_parts), cutting rows where a share
+ *                ends; cut rows leave fp32 partials that a second kernel
+ *                merges.  Every workgroup then streams the same number of
+ *                keys whatever the mix of context lengths (one long row among
+ *                short ones is spread over the whole chip).
+ *   workspace    device buffer of at least paged_decode_workspace_size(...)
+ *                bytes for the same num_splits and flags (may be NULL when
+ *                that size is 0); contents on entry do not matter and are
+ *                left undefined
  *   out          bf16 [batch][num_q_heads][head_dim]
  *   lse          fp32 [batch][num_q_heads]
  *
- * Results are bitwise reproducible for identical inputs and split count.
+ * Results are bitwise reproducible for identical inputs, schedule and device
+ * (the balanced schedule's cut points depend on the compute-unit count).
  * batch == 0 is a valid no-op.  Requirements: head_dim 64 or 128,
  * num_q_heads a multiple of num_kv_heads with at most 16 query heads per
  * KV head, page_size a power of two >= 16, scale finite and > 0.

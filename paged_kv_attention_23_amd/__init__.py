@@ -5,7 +5,7 @@ libpkv.so (include/pkv.h):
 
   paged_kv_append      scatter new tokens' K/V into their pages
   paged_decode_attn    one query token per row over its paged keys
-                       (single pass or split-K + log-sum-exp merge,
+                       (single pass, per-row or balanced split-K + merge,
                        contiguous-page fast path)
   packed_prefill_attn  document-causal attention over packed prompts
 
@@ -15,12 +15,14 @@ C calls and nothing else.
 from ._binding import (  # noqa: F401
     LIB_PATH,
     PKV_F_ASSUME_CONTIGUOUS,
+    PKV_F_BALANCED,
     PKV_F_NO_CONTIG_DETECT,
     PKV_MAX_SPLITS,
     last_error,
     load_library,
     packed_prefill_attn,
     paged_decode_attn,
+    paged_decode_balanced_parts,
     paged_decode_num_splits,
     paged_decode_workspace_size,
     paged_kv_append,

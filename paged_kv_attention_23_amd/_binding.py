@@ -41,6 +41,7 @@ def _header_constants():
 _C = _header_constants()
 PKV_F_ASSUME_CONTIGUOUS = _C["PKV_F_ASSUME_CONTIGUOUS"]
 PKV_F_NO_CONTIG_DETECT = _C["PKV_F_NO_CONTIG_DETECT"]
+PKV_F_BALANCED = _C["PKV_F_BALANCED"]
 PKV_MAX_SPLITS = _C["PKV_MAX_SPLITS"]
 
 
@@ -56,10 +57,12 @@ def load_library(path: str = LIB_PATH):
     L.paged_kv_append.argtypes = [_P, _P, _I32, _I32, _I32, _I32, _P, _I32, _I32, _P, _P, _I32,
                                   _P, _P, _P]
     L.paged_kv_append.restype = ctypes.c_int
-    L.paged_decode_workspace_size.argtypes = [_I32, _I32, _I32, _I32]
+    L.paged_decode_workspace_size.argtypes = [_I32, _I32, _I32, _I32, _I32, ctypes.c_uint32]
     L.paged_decode_workspace_size.restype = ctypes.c_size_t
     L.paged_decode_num_splits.argtypes = [_I32, _I32, _I32]
     L.paged_decode_num_splits.restype = _I32
+    L.paged_decode_balanced_parts.argtypes = [_I32, _I32, _I32]
+    L.paged_decode_balanced_parts.restype = _I32
     L.paged_decode_attn.argtypes = [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _I32, _I32, _P, _P,
                                     _I32, _I32, ctypes.c_float, _I32, _I32, ctypes.c_uint32, _P,
                                     ctypes.c_size_t, _P, _P, _P]
@@ -126,12 +129,18 @@ def paged_kv_append(k_pool: torch.Tensor, v_pool: torch.Tensor, page_table: torc
     _check(rc, "paged_kv_append")
 
 
-def paged_decode_workspace_size(batch: int, num_q_heads: int, head_dim: int, num_splits: int) -> int:
-    return int(load_library().paged_decode_workspace_size(batch, num_q_heads, head_dim, num_splits))
+def paged_decode_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                                num_splits: int = 0, flags: int = 0) -> int:
+    return int(load_library().paged_decode_workspace_size(batch, num_q_heads, num_kv_heads,
+                                                          head_dim, num_splits, flags))
 
 
 def paged_decode_num_splits(batch: int, num_kv_heads: int, max_kv_len: int) -> int:
     return int(load_library().paged_decode_num_splits(batch, num_kv_heads, max_kv_len))
+
+
+def paged_decode_balanced_parts(batch: int, num_kv_heads: int, max_kv_len: int) -> int:
+    return int(load_library().paged_decode_balanced_parts(batch, num_kv_heads, max_kv_len))
 
 
 def paged_decode_attn(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
@@ -142,8 +151,10 @@ def paged_decode_attn(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tenso
                       stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Decode attention; returns (out bf16 [B, H_q, D], lse fp32 [B, H_q]).
 
-    With num_splits = 0 the library picks the split count; the workspace
-    (uint8 tensor) is allocated here when not given and the plan needs one.
+    num_splits = 0 picks the per-row split count automatically, 1 is a single
+    pass, >1 per-row splits; flags |= PKV_F_BALANCED (with num_splits = 0)
+    selects the balanced schedule.  The workspace (uint8 tensor) is allocated
+    here when not given and the schedule needs one.
     """
     L = load_library()
     B, H_q, D = q.shape
@@ -153,12 +164,8 @@ def paged_decode_attn(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tenso
     num_slots, max_blocks = page_table.shape
     if batch_idx.shape[0] != B or kv_len.shape[0] != B:
         raise ValueError("batch_idx and kv_len must have one entry per row")
-    S = num_splits
-    if S == 0:
-        cap = max_blocks * page_size
-        bound = cap if (max_kv_len <= 0 or max_kv_len > cap) else max_kv_len
-        S = paged_decode_num_splits(B, H_kv, bound)
-    need = paged_decode_workspace_size(B, H_q, D, S)
+    S = int(num_splits)
+    need = paged_decode_workspace_size(B, H_q, H_kv, D, S, int(flags))
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr, ws_bytes = (0, 0) if workspace is None else (workspace.data_ptr(), workspace.numel())

@@ -223,42 +223,47 @@ __device__ __forceinline__ void compute_tile(const u32x4 (&k)[2][D / 32], int kt
   }
 }
 
-// Result of a unit with no valid key: O = +0, LSE = -inf (single pass), or a
-// partial with LSE = -inf that the merge gives weight zero.
-__device__ void write_empty(const DecodeArgs &a, int r, int g, int sp) {
-  const int pairs = a.G * (a.D >> 1);
+// Where one piece's result goes: G rows of D values (row stride D) and G
+// log-sum-exps (natural log).  Final results are bf16 rows of the output;
+// partial results are normalised fp32 rows in the workspace.
+struct PieceOut {
+  void *o;
+  float *lse;
+  bool final_;
+};
+
+__device__ __forceinline__ PieceOut final_out(const DecodeArgs &a, int r, int g) {
+  const int64_t rh = (int64_t)r * a.H_q + (int64_t)g * a.G;
+  return PieceOut{a.out + rh * a.D, a.lse + rh, true};
+}
+
+// A piece with no valid key: O = +0, LSE = -inf (a partial with LSE = -inf
+// gets weight zero in the merge).
+__device__ void write_empty(const PieceOut &dst, int G, int D) {
+  const int pairs = G * (D >> 1);
   for (int idx = threadIdx.x; idx < pairs; idx += kDecThreads) {
-    const int h = g * a.G + idx / (a.D >> 1);
-    const int d = 2 * (idx % (a.D >> 1));
-    const int64_t rh = (int64_t)r * a.H_q + h;
-    if (a.num_splits == 1) {
-      *reinterpret_cast<uint32_t *>(a.out + rh * a.D + d) = 0u;
-      if (d == 0) a.lse[rh] = -INFINITY;
-    } else {
-      const int64_t prh = (int64_t)sp * a.B * a.H_q + rh;
-      *reinterpret_cast<f32x2 *>(a.o_part + prh * a.D + d) = f32x2{0.f, 0.f};
-      if (d == 0) a.lse_part[prh] = -INFINITY;
-    }
+    const int hh = idx / (D >> 1);
+    const int d = 2 * (idx % (D >> 1));
+    if (dst.final_)
+      *reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(dst.o) + hh * D + d) = 0u;
+    else
+      *reinterpret_cast<f32x2 *>(reinterpret_cast<float *>(dst.o) + hh * D + d) = f32x2{0.f, 0.f};
+    if (d == 0) dst.lse[hh] = -INFINITY;
   }
 }
 
+// Attention of the G query heads of KV head g in row r over the row's keys
+// [lo, hi) (0 <= lo < hi <= n), all four waves of the workgroup together.
+// s is the row's slot (valid).  Ends with a workgroup barrier, so the caller
+// may start another piece right away.
 template <int D>
-__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(2)))
-void decode_kernel(DecodeArgs a) {
+__device__ void decode_piece(const DecodeArgs &a, char *smem, int r, int g, int s, int lo, int hi,
+                             const PieceOut &dst, int lane, int wave) {
   using Gm = DecGeom<D>;
-  __shared__ __attribute__((aligned(16))) char smem[Gm::kSmemBytes];
-
-  // blockIdx.x enumerates (split, KV head, row), split fastest.
-  const int sp = blockIdx.x % a.num_splits;
-  const int g = (blockIdx.x / a.num_splits) % a.H_kv;
-  const int r = blockIdx.x / (a.num_splits * a.H_kv);
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
   const int hl = lane & 15, lg = lane >> 4;
   const int G = a.G;
 
-  // Q^T as B operands: column hl = query head g*G + hl (zero past G).  Issued
-  // first: it does not depend on the slot, so it overlaps the row lookups.
+  // Q^T as B operands: column hl = query head g*G + hl (zero past G).
   bf16x8 qop[Gm::kDChunks];
   {
     const uint16_t *qr = a.q + ((int64_t)r * a.H_q + g * G + hl) * D + 8 * lg;
@@ -270,21 +275,7 @@ void decode_kernel(DecodeArgs a) {
     }
   }
 
-  const int s = a.batch_idx[r];
-  int n = a.kv_len[r];
-  n = min(n, a.max_blocks << a.page_shift);
-  const bool pad = (s <= 0) || (s >= a.num_slots) || (n <= 0);
-  // Split sp covers an equal share of this row's keys, in whole 32-key tiles.
-  const int chunk = ((n + a.num_splits - 1) / a.num_splits + kTileKeys - 1) & ~(kTileKeys - 1);
-  const int64_t lo64 = (int64_t)sp * chunk;
-  const int lo = (int)min(lo64, (int64_t)n);
-  const int hi = (sp == a.num_splits - 1) ? n : (int)min((int64_t)n, lo64 + chunk);
-  if (pad || lo >= hi) {
-    write_empty(a, r, g, sp);
-    return;
-  }
-
-  // Where this unit's keys live; detect consecutive page ids (one wave vote).
+  // Where this piece's keys live; detect consecutive page ids (one wave vote).
   RowCtx c;
   c.pt_row = a.page_table + (int64_t)s * a.max_blocks;
   c.page_shift = a.page_shift;
@@ -394,23 +385,183 @@ void decode_kernel(DecodeArgs a) {
     }
     const float inv = (L > 0.f) ? 1.f / L : 0.f;
     const float lse_nat = (L > 0.f) ? (M + log2f(L)) * kLn2 : -INFINITY;
-    const int64_t rh = (int64_t)r * a.H_q + g * G + hh;
-    if (a.num_splits == 1) {
-      *reinterpret_cast<uint32_t *>(a.out + rh * D + d) = pack_bf16x2(o0 * inv, o1 * inv);
-      if (d == 0) a.lse[rh] = lse_nat;
-    } else {
-      const int64_t prh = (int64_t)sp * a.B * a.H_q + rh;
-      *reinterpret_cast<f32x2 *>(a.o_part + prh * D + d) = f32x2{o0 * inv, o1 * inv};
-      if (d == 0) a.lse_part[prh] = lse_nat;
-    }
+    if (dst.final_)
+      *reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(dst.o) + hh * D + d) =
+          pack_bf16x2(o0 * inv, o1 * inv);
+    else
+      *reinterpret_cast<f32x2 *>(reinterpret_cast<float *>(dst.o) + hh * D + d) =
+          f32x2{o0 * inv, o1 * inv};
+    if (d == 0) dst.lse[hh] = lse_nat;
   }
+  __syncthreads();  // the LDS is free for the next piece
 }
 
-// Merge of split partials: one wave per (row, query head).
+// Valid keys of row r (0 for padding rows: slot 0 / out of range / kv_len <= 0),
+// clamped to the page table's capacity.
+__device__ __forceinline__ int row_keys(const DecodeArgs &a, int r, int &slot) {
+  const int s = a.batch_idx[r];
+  const int n = min(a.kv_len[r], a.max_blocks << a.page_shift);
+  slot = s;
+  return (s <= 0 || s >= a.num_slots || n <= 0) ? 0 : n;
+}
+
+// Per-row schedule: blockIdx.x enumerates (split, KV head, row), split
+// fastest; split sp of a row covers an equal share of its keys in whole
+// 32-key tiles.  With one split the result is final, else a partial.
+template <int D>
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_rows_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[DecGeom<D>::kSmemBytes];
+  const int S = a.num_splits;
+  const int sp = blockIdx.x % S;
+  const int g = (blockIdx.x / S) % a.H_kv;
+  const int r = blockIdx.x / (S * a.H_kv);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+
+  int s;
+  const int n = row_keys(a, r, s);
+  const int chunk = ((n + S - 1) / S + kTileKeys - 1) & ~(kTileKeys - 1);
+  const int64_t lo64 = (int64_t)sp * chunk;
+  const int lo = (int)min(lo64, (int64_t)n);
+  const int hi = (sp == S - 1) ? n : (int)min((int64_t)n, lo64 + chunk);
+  PieceOut dst = final_out(a, r, g);
+  if (S > 1) {
+    const int64_t prh = ((int64_t)sp * a.B + r) * a.H_q + (int64_t)g * a.G;
+    dst = PieceOut{a.o_part + prh * D, a.lse_part + prh, false};
+  }
+  if (lo >= hi) {
+    write_empty(dst, a.G, D);
+    return;
+  }
+  decode_piece<D>(a, smem, r, g, s, lo, hi, dst, lane, wave);
+}
+
+__device__ __forceinline__ int64_t readlane64(int64_t v, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)v >> 32), l);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Sum over the wave, returned as a wave-uniform (scalar) value.
+__device__ __forceinline__ int64_t wave_sum64(int64_t v) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) v += __shfl_xor(v, m, kWave);
+  return readlane64(v, 0);
+}
+
+__device__ __forceinline__ int64_t wave_incl_scan64(int64_t v, int lane) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int64_t u = __shfl_up(v, off, kWave);
+    if (lane >= off) v += u;
+  }
+  return v;
+}
+
+// Balanced schedule (flash-decoding with split points balanced across rows).
+// For KV head g, the 32-key tiles of all rows, row after row, form one list of
+// TT tiles; workgroup w takes tiles [TT*w/W', TT*(w+1)/W') with W' = min(W, TT),
+// so every workgroup streams the same number of tiles whatever the row
+// lengths.  A row wholly inside one range is written as the final result; a
+// row cut by range boundaries leaves one normalised partial per workgroup, in
+// slot 0 (the row holding the range's first tile) or slot 1 (the row holding
+// its last tile), and the workgroup holding the row's first tile records the
+// row in its descriptor for the merge kernel.  Padding rows (no tiles) are
+// written by the workgroup whose range holds their position in the list (the
+// last workgroup for positions at the end).  Every workgroup recomputes the
+// row prefix sums itself (batch_idx / kv_len are a few cached lines), so the
+// plan needs no extra launch.  Everything but the lanes' prefix ends is kept
+// in scalar registers across the pieces.
+template <int D>
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_balanced_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[DecGeom<D>::kSmemBytes];
+  const int g = blockIdx.x % a.H_kv;
+  const int w = blockIdx.x / a.H_kv;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int W = a.num_splits;
+
+  // Pass 1: total tiles.  The lanes' rows of the first 64-row chunk stay in
+  // registers for pass 2 (a batch of up to 64 rows is read once).
+  int64_t TT = 0;
+  int s_first = 0, n_first = 0;
+  for (int cb = 0; cb < a.B; cb += kWave) {
+    int s = 0, n = 0;
+    if (cb + lane < a.B) n = row_keys(a, cb + lane, s);
+    if (cb == 0) {
+      s_first = s;
+      n_first = n;
+    }
+    TT += wave_sum64((n + kTileKeys - 1) / kTileKeys);
+  }
+  const int We = (int)min<int64_t>(W, TT);
+  const int last_owner = max(We - 1, 0);
+  int desc_r = -1, desc_slot = 0, desc_last = 0;
+  if (w < We || w == last_owner) {
+    const int64_t t0 = We ? TT * w / We : 0;
+    const int64_t t1 = We ? TT * (w + 1) / We : 0;
+    int64_t carry = 0;
+    for (int cb = 0; cb < a.B && carry <= t1; cb += kWave) {
+      const int r = cb + lane;
+      int s = s_first, n = n_first;
+      if (cb != 0) {
+        n = 0;
+        if (r < a.B) n = row_keys(a, r, s);
+      }
+      uint64_t mask;
+      int64_t pe;  // end of the lane's row in the tile list
+      {
+        const int tiles = (n + kTileKeys - 1) / kTileKeys;
+        pe = carry + wave_incl_scan64(tiles, lane);
+        const int64_t ps = pe - tiles;
+        bool mine = false;
+        if (r < a.B) {
+          if (tiles > 0) mine = pe > t0 && ps < t1;
+          else mine = (ps >= t0 && ps < t1) || (ps == TT && w == last_owner);
+        }
+        mask = __ballot(mine);
+      }
+      carry = readlane64(pe, kWave - 1);
+      while (mask) {
+        const int j = __builtin_ctzll(mask);
+        mask &= mask - 1;
+        const int rr = cb + j;
+        const int sj = __builtin_amdgcn_readlane(s, j);
+        const int nj = __builtin_amdgcn_readlane(n, j);
+        const int64_t ej = readlane64(pe, j);
+        const int64_t pj = ej - (nj + kTileKeys - 1) / kTileKeys;
+        if (nj == 0) {
+          write_empty(final_out(a, rr, g), a.G, D);
+          continue;
+        }
+        const int64_t klo = max(pj, t0), khi = min(ej, t1);
+        const int lo = (int)(klo - pj) * kTileKeys;
+        const int hi = (int)min<int64_t>(nj, (khi - pj) * kTileKeys);
+        PieceOut dst = final_out(a, rr, g);
+        if (pj < t0 || ej > t1) {
+          const int slot = (pj <= t0) ? 0 : 1;
+          const int64_t pidx = (((int64_t)g * W + w) * 2 + slot) * a.G;
+          dst = PieceOut{a.o_part + pidx * D, a.lse_part + pidx, false};
+          if (pj >= t0) {  // this range holds the row's first tile: it owns the merge
+            desc_r = rr;
+            desc_slot = slot;
+            desc_last = (int)((ej * We + TT - 1) / TT) - 1;  // range holding tile ej-1
+          }
+        }
+        decode_piece<D>(a, smem, rr, g, sj, lo, hi, dst, lane, wave);
+      }
+    }
+  }
+  if (threadIdx.x == 0) a.desc[(int64_t)g * W + w] = int4{desc_r, desc_slot, desc_last, 0};
+}
+
+// Merge of per-row split partials: one wave per (row, query head).
 //   M = max_s L_s; LSE = M + ln sum_s exp(L_s - M); O = sum_s exp(L_s - LSE) O_s
 // Partials with L_s = -inf carry weight zero and are not read.
 template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) void merge_rows_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t rh = (int64_t)blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
   const int64_t nrh = (int64_t)a.B * a.H_q;
@@ -453,21 +604,84 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
   if (lane == 0) a.lse[rh] = L;
 }
 
+// Merge of the balanced schedule's cut rows: one workgroup per (KV head,
+// range b).  Range b's descriptor names the cut row whose first tile it holds
+// (if any) and the last range that row reaches; the partials are those of
+// ranges b .. last (slot desc.y for b, slot 0 for the others).  Each thread
+// owns two adjacent outputs of one query head and folds the partials in
+// range order with a running maximum:
+//   M' = max(M, L_w);  S' = S e^(M-M') + e^(L_w-M');  O' = O e^(M-M') + e^(L_w-M') O_w
+// which ends at O = sum_w e^(L_w) O_w / sum_w e^(L_w) and LSE = M + ln S.
+// The loads of different ranges do not depend on each other, so unrolling
+// keeps several in flight.
+template <int D>
+__global__ __launch_bounds__(256) void merge_balanced_kernel(DecodeArgs a) {
+  const int W = a.num_splits;
+  const int g = blockIdx.x % a.H_kv;
+  const int b = blockIdx.x / a.H_kv;
+  const int4 desc = a.desc[(int64_t)g * W + b];
+  const int r = desc.x;
+  if (r < 0) return;
+  const int wl = min(desc.z, W - 1);
+  const int G = a.G;
+  const int pairs = G * (D / 2);
+  for (int idx = threadIdx.x; idx < pairs; idx += 256) {
+    const int hh = idx / (D / 2);
+    const int d = 2 * (idx % (D / 2));
+    float M = -INFINITY, S = 0.f, o0 = 0.f, o1 = 0.f;
+#pragma unroll 4
+    for (int w = b; w <= wl; ++w) {
+      const int slot = (w == b) ? desc.y : 0;
+      const int64_t pidx = (((int64_t)g * W + w) * 2 + slot) * G + hh;
+      const float L = a.lse_part[pidx];
+      const f32x2 ov = *reinterpret_cast<const f32x2 *>(a.o_part + pidx * D + d);
+      if (L == -INFINITY) continue;
+      const float Mn = fmaxf(M, L);
+      const float keep = (M == -INFINITY) ? 0.f : expf(M - Mn);
+      const float add = expf(L - Mn);
+      S = S * keep + add;
+      o0 = o0 * keep + add * ov[0];
+      o1 = o1 * keep + add * ov[1];
+      M = Mn;
+    }
+    const float inv = (S > 0.f) ? 1.f / S : 0.f;
+    const int64_t rh = (int64_t)r * a.H_q + (int64_t)g * G + hh;
+    *reinterpret_cast<uint32_t *>(a.out + rh * D + d) = pack_bf16x2(o0 * inv, o1 * inv);
+    if (d == 0) a.lse[rh] = (S > 0.f) ? M + logf(S) : -INFINITY;
+  }
+}
+
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   if (a.B == 0) return hipSuccess;
-  const dim3 grid((unsigned)((int64_t)a.num_splits * a.H_kv * a.B));
-  if (a.D == 128)
-    hipLaunchKernelGGL(decode_kernel<128>, grid, dim3(kDecThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(decode_kernel<64>, grid, dim3(kDecThreads), 0, stream, a);
+  const bool balanced = a.balanced != 0;
+  const dim3 grid((unsigned)((int64_t)a.num_splits * a.H_kv * (balanced ? 1 : a.B)));
+  if (balanced) {
+    if (a.D == 128)
+      hipLaunchKernelGGL(decode_balanced_kernel<128>, grid, dim3(kDecThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL(decode_balanced_kernel<64>, grid, dim3(kDecThreads), 0, stream, a);
+  } else {
+    if (a.D == 128)
+      hipLaunchKernelGGL(decode_rows_kernel<128>, grid, dim3(kDecThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL(decode_rows_kernel<64>, grid, dim3(kDecThreads), 0, stream, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_splits == 1) return e;
-  const int64_t nrh = (int64_t)a.B * a.H_q;
-  const unsigned mblocks = (unsigned)((nrh + 3) / 4);
-  if (a.D == 128)
-    hipLaunchKernelGGL(merge_kernel<128>, dim3(mblocks), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(merge_kernel<64>, dim3(mblocks), dim3(256), 0, stream, a);
+  if (balanced) {
+    const unsigned mblocks = (unsigned)((int64_t)a.H_kv * (a.num_splits - 1));  // last range owns no merge
+    if (a.D == 128)
+      hipLaunchKernelGGL(merge_balanced_kernel<128>, dim3(mblocks), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL(merge_balanced_kernel<64>, dim3(mblocks), dim3(256), 0, stream, a);
+  } else {
+    const int64_t nrh = (int64_t)a.B * a.H_q;
+    const unsigned mblocks = (unsigned)((nrh + 3) / 4);
+    if (a.D == 128)
+      hipLaunchKernelGGL(merge_rows_kernel<128>, dim3(mblocks), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL(merge_rows_kernel<64>, dim3(mblocks), dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

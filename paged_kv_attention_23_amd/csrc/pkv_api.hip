@@ -75,20 +75,42 @@ int device_cus() {
 
 constexpr int kMinSplitKeys = 256;
 
-int32_t auto_splits(int32_t batch, int32_t num_kv_heads, int32_t max_kv_len, int cus) {
-  // One workgroup per (row, KV head) already fills the chip when there are at
-  // least as many units as compute units; splitting then only adds the merge
-  // pass.  Below that, split so that roughly one unit lands on every CU,
-  // keeping at least kMinSplitKeys keys per split.
+// Per-row schedule, automatic split count.  One workgroup per (row, KV head)
+// already fills the chip when there are at least as many units as compute
+// units; splitting then only adds the merge pass.  Below that, split so that
+// roughly one unit lands on every CU, keeping at least kMinSplitKeys keys per
+// split.
+int32_t auto_splits(int32_t batch, int32_t num_kv_heads, int32_t kv_bound, int cus) {
   const int64_t units = (int64_t)batch * num_kv_heads;
-  if (units <= 0 || max_kv_len <= 0 || units >= cus) return 1;
+  if (units <= 0 || kv_bound <= 0 || units >= cus) return 1;
   int64_t s = (cus + units / 2) / units;
-  const int64_t by_len = max_kv_len / kMinSplitKeys;
+  const int64_t by_len = kv_bound / kMinSplitKeys;
   if (s > by_len) s = by_len;
   if (s > PKV_MAX_SPLITS) s = PKV_MAX_SPLITS;
   if (s < 1) s = 1;
   return (int32_t)s;
 }
+
+// Balanced schedule: workgroups per KV head.  Two decode workgroups fit on a
+// compute unit, so 2*CUs workgroups in all fill the chip in one wave; fewer
+// when the batch cannot give each at least a few tiles (four 32-key tiles, one
+// per wave), but never fewer than one per row.
+int32_t balanced_max_parts(int32_t num_kv_heads, int cus) {
+  int64_t w = (2 * (int64_t)cus) / num_kv_heads;
+  if (w > 4096) w = 4096;
+  return (int32_t)(w < 1 ? 1 : w);
+}
+
+int32_t balanced_parts(int32_t batch, int32_t num_kv_heads, int32_t kv_bound, int cus) {
+  const int64_t wmax = balanced_max_parts(num_kv_heads, cus);
+  const int64_t tiles = (int64_t)batch * ((kv_bound + 31) / 32);
+  int64_t w = (tiles + 3) / 4;
+  if (w < batch) w = batch;
+  if (w > wmax) w = wmax;
+  return (int32_t)(w < 1 ? 1 : w);
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 }  // namespace
 
@@ -130,16 +152,31 @@ int paged_kv_append(void *k_pool, void *v_pool, int32_t num_pages, int32_t page_
   return launch_status(pkv::launch_kv_append(a, (hipStream_t)stream), "paged_kv_append launch");
 }
 
-size_t paged_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t head_dim,
-                                   int32_t num_splits) {
-  if (num_splits <= 1 || batch <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
-  const size_t rows = (size_t)num_splits * (size_t)batch * (size_t)num_q_heads;
-  const size_t o_bytes = (rows * (size_t)head_dim * sizeof(float) + 255) & ~(size_t)255;
-  return o_bytes + rows * sizeof(float);
+size_t paged_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t num_splits, uint32_t flags) {
+  if (num_splits < 0 || batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      num_q_heads % num_kv_heads != 0)
+    return 0;
+  if (flags & PKV_F_BALANCED) {
+    const size_t parts = (size_t)num_kv_heads * balanced_max_parts(num_kv_heads, device_cus()) * 2;
+    const size_t rows = parts * (size_t)(num_q_heads / num_kv_heads);
+    return align256(rows * (size_t)head_dim * sizeof(float)) + align256(rows * sizeof(float)) +
+           parts / 2 * 4 * sizeof(int32_t);
+  }
+  // automatic: the largest count auto_splits can pick for this batch, whatever the lengths
+  const int32_t S = num_splits ? num_splits : auto_splits(batch, num_kv_heads, INT32_MAX, device_cus());
+  if (S <= 1) return 0;
+  const size_t rows = (size_t)S * (size_t)batch * (size_t)num_q_heads;
+  return align256(rows * (size_t)head_dim * sizeof(float)) + rows * sizeof(float);
 }
 
 int32_t paged_decode_num_splits(int32_t batch, int32_t num_kv_heads, int32_t max_kv_len) {
   return auto_splits(batch, num_kv_heads, max_kv_len, device_cus());
+}
+
+int32_t paged_decode_balanced_parts(int32_t batch, int32_t num_kv_heads, int32_t max_kv_len) {
+  if (batch <= 0 || num_kv_heads <= 0) return 1;
+  return balanced_parts(batch, num_kv_heads, max_kv_len > 0 ? max_kv_len : 1, device_cus());
 }
 
 int paged_decode_attn(const void *q, const void *k_pool, const void *v_pool, int32_t num_pages,
@@ -161,7 +198,7 @@ int paged_decode_attn(const void *q, const void *k_pool, const void *v_pool, int
   if (!(scale > 0.f) || isinf(scale)) return fail(PKV_E_SHAPE, "scale must be finite and positive");
   if (num_splits < 0 || num_splits > PKV_MAX_SPLITS)
     return fail(PKV_E_SPLITS, "num_splits must be in [0, %d] (got %d)", PKV_MAX_SPLITS, num_splits);
-  if (flags & ~(uint32_t)(PKV_F_ASSUME_CONTIGUOUS | PKV_F_NO_CONTIG_DETECT))
+  if (flags & ~(uint32_t)(PKV_F_ASSUME_CONTIGUOUS | PKV_F_NO_CONTIG_DETECT | PKV_F_BALANCED))
     return fail(PKV_E_SHAPE, "unknown flag bits 0x%x", flags);
   if ((int64_t)batch * num_kv_heads * PKV_MAX_SPLITS > INT32_MAX)
     return fail(PKV_E_SHAPE, "batch*num_kv_heads too large (got %d*%d)", batch, num_kv_heads);
@@ -175,22 +212,46 @@ int paged_decode_attn(const void *q, const void *k_pool, const void *v_pool, int
 
   const int32_t cap = max_blocks * page_size;
   const int32_t kv_bound = (max_kv_len <= 0 || max_kv_len > cap) ? cap : max_kv_len;
-  int32_t S = num_splits;
-  if (S == 0) S = auto_splits(batch, num_kv_heads, kv_bound, device_cus());
+  const bool balanced = (flags & PKV_F_BALANCED) != 0;
+  if (balanced && num_splits != 0)
+    return fail(PKV_E_SPLITS, "PKV_F_BALANCED chooses its own split points: num_splits must be 0 (got %d)",
+                num_splits);
+  int32_t S;
+  if (balanced) {
+    S = balanced_parts(batch, num_kv_heads, kv_bound, device_cus());
+    // The balanced plan forms products (tiles in the list) * (workgroups) in int64.
+    if ((double)batch * ((cap + 31) / 32) * S > 4.0e18)
+      return fail(PKV_E_SHAPE, "batch*max_blocks*page_size too large for the balanced schedule");
+  } else {
+    S = num_splits ? num_splits : auto_splits(batch, num_kv_heads, kv_bound, device_cus());
+  }
 
   pkv::DecodeArgs a;
   a.o_part = nullptr;
   a.lse_part = nullptr;
+  a.desc = nullptr;
   if (S > 1) {
-    const size_t need = paged_decode_workspace_size(batch, num_q_heads, head_dim, S);
+    const size_t need = paged_decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim,
+                                                    balanced ? 0 : S, flags);
     if (!workspace || workspace_bytes < need)
-      return fail(PKV_E_WORKSPACE, "paged_decode_attn: %d splits need %zu workspace bytes (got %zu%s)",
-                  S, need, workspace_bytes, workspace ? "" : ", NULL");
+      return fail(PKV_E_WORKSPACE, "paged_decode_attn: %s needs %zu workspace bytes (got %zu%s)",
+                  balanced ? "the balanced schedule" : "this split count", need, workspace_bytes,
+                  workspace ? "" : ", NULL");
     if (!aligned16(workspace))
       return fail(PKV_E_ALIGN, "paged_decode_attn: workspace must be 16-byte aligned");
-    const size_t rows = (size_t)S * batch * num_q_heads;
-    a.o_part = (float *)workspace;
-    a.lse_part = (float *)((char *)workspace + ((rows * head_dim * sizeof(float) + 255) & ~(size_t)255));
+    char *ws = (char *)workspace;
+    if (balanced) {
+      const size_t rows = (size_t)num_kv_heads *
+                          balanced_max_parts(num_kv_heads, device_cus()) * 2 *
+                          (size_t)(num_q_heads / num_kv_heads);
+      a.o_part = (float *)ws;
+      a.lse_part = (float *)(ws + align256(rows * head_dim * sizeof(float)));
+      a.desc = (int4 *)(ws + align256(rows * head_dim * sizeof(float)) + align256(rows * sizeof(float)));
+    } else {
+      const size_t rows = (size_t)S * batch * num_q_heads;
+      a.o_part = (float *)ws;
+      a.lse_part = (float *)(ws + align256(rows * head_dim * sizeof(float)));
+    }
   }
   a.q = (const uint16_t *)q;
   a.k_pool = (const uint16_t *)k_pool;
@@ -209,6 +270,7 @@ int paged_decode_attn(const void *q, const void *k_pool, const void *v_pool, int
   a.G = num_q_heads / num_kv_heads;
   a.D = head_dim;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.balanced = (balanced && S > 1) ? 1 : 0;
   a.num_splits = S;
   a.contig_mode = (flags & PKV_F_NO_CONTIG_DETECT) ? 2 : (flags & PKV_F_ASSUME_CONTIGUOUS) ? 1 : 0;
   a.out = (uint16_t *)out;

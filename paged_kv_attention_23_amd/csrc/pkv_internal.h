@@ -25,9 +25,13 @@ struct DecodeArgs {
   int32_t num_pages, page_shift, num_slots, max_blocks;
   int32_t B, H_q, H_kv, G, D;
   float scale_log2;                // scale * log2(e)
-  int32_t num_splits;              // key splits per row (each gets an equal share)
+  int32_t balanced;                // 1: balanced schedule, 0: per-row splits
+  int32_t num_splits;              // per-row: splits per row; balanced: workgroups per KV head (W)
   int32_t contig_mode;             // 0 detect per row, 1 assume contiguous, 2 never
-  float *o_part, *lse_part;        // split partials [S][B][H_q][D], [S][B][H_q]
+  // Partials.  Per-row: [S][B][H_q][D] and [S][B][H_q].  Balanced: [H_kv][W][2][G][D],
+  // [H_kv][W][2][G] and one descriptor per (KV head, workgroup) in desc.
+  float *o_part, *lse_part;
+  int4 *desc;
   uint16_t *out;                   // [B][H_q][D] bf16
   float *lse;                      // [B][H_q]
 };

@@ -138,8 +138,13 @@ def test_append_skips_and_invalid_entries():
 
 
 # ----------------------------------------------------------------------------- decode
-SPLITS = [1, 2, 3, 7, 0]
+SPLITS = [1, 2, 3, 7, 0, "balanced"]
 MODES = {"detect": 0, "walk": pkv.PKV_F_NO_CONTIG_DETECT}
+
+
+def _sched(splits):
+    """(num_splits, extra flags) of a SPLITS entry."""
+    return (0, pkv.PKV_F_BALANCED) if splits == "balanced" else (splits, 0)
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4])
@@ -151,7 +156,8 @@ def test_decode_parity(cfg, splits, mode):
         pytest.skip("covered by the other split counts")
     d = _dev(cfg)
     _, _, out_ref, lse_ref = _ref(cfg)
-    out, lse = d.decode(num_splits=splits, flags=MODES[mode])
+    S, extra = _sched(splits)
+    out, lse = d.decode(num_splits=S, flags=MODES[mode] | extra)
     torch.cuda.synchronize()
     check_close(out, lse, out_ref, lse_ref, f"cfg{cfg}/S{splits}/{mode}")
 
@@ -217,15 +223,16 @@ SMALL = [
 
 
 @pytest.mark.parametrize("spec", SMALL, ids=[f"seed{s[0]}" for s in SMALL])
-@pytest.mark.parametrize("splits", [1, 2, 5, 0])
+@pytest.mark.parametrize("splits", [1, 2, 5, 0, "balanced"])
 def test_decode_edge_shapes(spec, splits):
     seed, H_q, H_kv, D, ps, lens, layout = spec
     _print_case(f"decode small seed={seed} splits={splits}")
     c = _small_case(seed, H_q, H_kv, D, ps, lens, layout)
     out_ref, lse_ref = oracle.decode_case(c)
     d = _Dev(c)
+    S, extra = _sched(splits)
     for mode in MODES.values():
-        out, lse = d.decode(num_splits=splits, flags=mode)
+        out, lse = d.decode(num_splits=S, flags=mode | extra)
         torch.cuda.synchronize()
         check_close(out, lse, out_ref, lse_ref, f"seed{seed}/S{splits}/flags{mode}")
 
@@ -242,6 +249,40 @@ def test_decode_kv_len_zero_and_empty_splits():
         check_close(out, lse, out_ref, lse_ref, f"kvlen0/S{S}")
         ob = host_bits(out)
         assert np.all(ob[[0, 3]] == 0)
+
+
+BALANCED = [
+    # (seed, H_q, H_kv, D, ps, lens, slots, max_kv_len passed)
+    (51, 8, 2, 128, 32, [0, 40, 3, 0], None, 0),               # fewer tiles than workgroups
+    (52, 8, 2, 64, 16, [0, 0, 0], None, 0),                     # no valid key at all
+    (53, 8, 2, 128, 16, [5000], None, 5000),                    # one row cut ~40 ways, > 64 blocks
+    (54, 32, 8, 128, 16, [int(x) for x in np.random.default_rng(54).integers(0, 300, 130)],
+     None, 300),                                                # two scan chunks, many cut rows
+    (55, 16, 4, 64, 64, [700, 1, 0, 33, 2000, 64, 65] * 9,
+     [0 if i % 5 == 2 else i + 1 for i in range(63)], 2000),    # padding slots interleaved
+]
+
+
+@pytest.mark.parametrize("spec", BALANCED, ids=[f"seed{s[0]}" for s in BALANCED])
+def test_decode_balanced_plans(spec):
+    """The balanced schedule (PKV_F_BALANCED) on plans that stress its cut points."""
+    seed, H_q, H_kv, D, ps, lens, slots, mkl = spec
+    _print_case(f"decode balanced seed={seed} B={len(lens)}")
+    c = _small_case(seed, H_q, H_kv, D, ps, lens, "shuffled", slots=slots)
+    out_ref, lse_ref = oracle.decode_case(c)
+    d = _Dev(c)
+    W = pkv.paged_decode_balanced_parts(c.B, c.H_kv, mkl if mkl else c.max_blocks * ps)
+    for mode in MODES.values():
+        out, lse = pkv.paged_decode_attn(d.q, d.k, d.v, d.pt, d.bi, d.kl, page_size=ps,
+                                         scale=float(c.scale), max_kv_len=mkl, num_splits=0,
+                                         flags=mode | pkv.PKV_F_BALANCED)
+        torch.cuda.synchronize()
+        check_close(out, lse, out_ref, lse_ref, f"balanced seed{seed} W={W} flags{mode}")
+        o2, l2 = pkv.paged_decode_attn(d.q, d.k, d.v, d.pt, d.bi, d.kl, page_size=ps,
+                                       scale=float(c.scale), max_kv_len=mkl, num_splits=0,
+                                       flags=mode | pkv.PKV_F_BALANCED)
+        torch.cuda.synchronize()
+        assert torch.equal(out, o2) and torch.equal(lse, l2)
 
 
 def test_decode_needles():

@@ -33,6 +33,7 @@ def test_exports_every_declared_symbol(lib):
     names = _declared()
     assert set(names) >= {"paged_kv_append", "paged_decode_attn", "packed_prefill_attn",
                           "paged_decode_workspace_size", "paged_decode_num_splits",
+                          "paged_decode_balanced_parts",
                           "pkv_last_error"}
     raw = ctypes.CDLL(LIB)
     for n in names:
@@ -42,6 +43,7 @@ def test_exports_every_declared_symbol(lib):
 def test_header_constants_parsed():
     assert B._C["PKV_OK"] == 0 and B._C["PKV_E_HIP"] == -6
     assert B.PKV_F_ASSUME_CONTIGUOUS == 1 and B.PKV_F_NO_CONTIG_DETECT == 2
+    assert B.PKV_F_BALANCED == 4
     assert B.PKV_MAX_SPLITS == 64
 
 
@@ -80,6 +82,8 @@ def _decode(lib, **kw):
     (dict(out=FAKE + 8), -3, "aligned"),
     (dict(kl=FAKE + 2), -3, "aligned"),
     (dict(splits=2), -4, "workspace"),
+    (dict(splits=2, flags=4), -5, "num_splits"),
+    (dict(splits=0, flags=4), -4, "workspace"),
     (dict(splits=2, ws=FAKE, ws_bytes=100), -4, "workspace"),
     (dict(splits=2, ws=FAKE + 4, ws_bytes=1 << 20), -3, "workspace"),
 ])
@@ -117,8 +121,39 @@ def test_prefill_checks(lib):
 
 def test_workspace_size(lib):
     ws = lib.paged_decode_workspace_size
-    assert ws(4, 32, 128, 1) == 0 and ws(4, 32, 128, 0) == 0
+    assert ws(4, 32, 8, 128, 1, 0) == 0
     rows = 3 * 2 * 4
     o_bytes = (rows * 128 * 4 + 255) // 256 * 256
-    assert ws(2, 4, 128, 3) == o_bytes + rows * 4
-    assert ws(0, 4, 128, 3) == 0
+    assert ws(2, 4, 2, 128, 3, 0) == o_bytes + rows * 4
+    assert ws(0, 4, 2, 128, 3, 0) == 0
+    assert ws(2, 5, 2, 128, 3, 0) == 0                 # H_q not a multiple of H_kv
+    # automatic: sized for the largest split count the heuristic can pick
+    s_max = lib.paged_decode_num_splits(2, 2, 1 << 30)
+    rows = s_max * 2 * 4
+    assert ws(2, 4, 2, 128, 0, 0) == (rows * 128 * 4 + 255) // 256 * 256 + rows * 4
+    assert ws(512, 32, 8, 128, 0, 0) == 0              # enough units: single pass
+    # balanced: partials for 2 slots per (KV head, workgroup), independent of the batch
+    w8 = lib.paged_decode_balanced_parts(100000, 8, 1 << 20)      # the cap: 2*CUs/H_kv
+    assert w8 >= 1
+    b = ws(64, 32, 8, 128, 0, 4)
+    assert b == ws(7, 32, 8, 128, 0, 4) > 0
+    rows = 8 * w8 * 2 * 4
+    assert b == (rows * 128 * 4 + 255) // 256 * 256 + (rows * 4 + 255) // 256 * 256 + 8 * w8 * 16
+
+
+def test_auto_splits(lib):
+    ns = lib.paged_decode_num_splits
+    assert ns(64, 8, 1024) == 1                        # 512 units fill the chip
+    assert ns(8, 8, 1536) == min(1536 // 256, round(256 / 64))
+    assert ns(1, 1, 100) == 1                          # too short to split
+    assert 1 <= ns(1, 1, 1 << 20) <= 64
+
+
+def test_balanced_parts(lib):
+    bp = lib.paged_decode_balanced_parts
+    wmax = bp(100000, 8, 1 << 20)
+    assert bp(100000, 1, 1 << 20) == min(8 * wmax, 4096)
+    assert bp(3, 2, 100) == 3                        # at least one workgroup per row
+    assert bp(1, 2, 5000) == -(-157 // 4)            # 157 tiles, four per workgroup
+    assert bp(64, 8, 1024) == wmax                   # enough tiles: the cap
+    assert bp(0, 8, 1024) == 1
