@@ -12,8 +12,9 @@
 //    G heads.  Tiles never straddle documents.
 //  * blockIdx enumerates (tile, KV head) with the KV head fastest; workgroups
 //    are dealt round-robin to the 8 XCDs, so with 8 KV heads each XCD serves
-//    one head and the query tiles of a document re-read its K/V from that
-//    XCD's L2.  Tiles are ordered longest first (largest key range first).
+//    one head.  Tiles are in document order (a document's tiles back to
+//    back, its longest key range first), so the query tiles of a document
+//    re-read its K/V from that XCD's L2 rather than from HBM.
 //  * Each of the 4 waves owns 32 of the 128 rows (two 16-column blocks).
 //    Scores are computed transposed, S^T[key][row] = K Q^T, so the score
 //    layout is directly the B operand P^T of O^T = V^T P^T (the same scheme
@@ -46,63 +47,40 @@ struct PfTile {
   int doc_start, q_lo, q_hi;
 };
 
-// Tile number -> (document, query tile), longest key range first: level j
-// holds query tile j of every document with more than j tiles, levels in
-// descending j, documents in order within a level.  Every wave computes this
-// redundantly.  Tile counts of up to 256 documents are loaded once into
-// registers (lane d of chunk c holds document 64*c + d), so each level is a
-// few ballots; longer document lists reload per level.
+// Tile number -> (document, query tile), document-major: the tiles of
+// document 0, then of document 1, ...; within a document the last query tile
+// (the longest key range) first.  Consecutive tiles of one KV head therefore
+// share their document's K/V, which stays in the XCD's L2 while its tiles
+// run.  Every wave computes this redundantly: one load of 64 document
+// lengths, a prefix sum and a ballot per 64 documents.
 __device__ __forceinline__ int ceil_div_qt(int x, int QT, int qt_shift) {
   return qt_shift >= 0 ? (x + QT - 1) >> qt_shift : (x + QT - 1) / QT;
 }
 
 __device__ bool find_tile(const int32_t *cu, int num_docs, int QT, int qt_shift, int tile, int lane,
                           PfTile &out) {
-  constexpr int kCached = 4;  // 64-document chunks held in registers
-  int tcount[kCached];
-  int jmax = 0;
-#pragma unroll
-  for (int c = 0; c < kCached; ++c) {
-    const int d = 64 * c + lane;
-    tcount[c] = (d < num_docs) ? ceil_div_qt(cu[d + 1] - cu[d], QT, qt_shift) : 0;
-  }
+  int base = 0;  // tiles of the documents before this chunk
   for (int d0 = 0; d0 < num_docs; d0 += kWave) {
     const int d = d0 + lane;
-    int t = 0;
-    if (d0 < kCached * kWave) {
+    const int t = (d < num_docs) ? ceil_div_qt(cu[d + 1] - cu[d], QT, qt_shift) : 0;
+    int incl = t;  // inclusive prefix sum of tile counts over the chunk
 #pragma unroll
-      for (int c = 0; c < kCached; ++c)
-        if (d0 == 64 * c) t = tcount[c];
-    } else if (d < num_docs) {
-      t = ceil_div_qt(cu[d + 1] - cu[d], QT, qt_shift);
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int u = __shfl_up(incl, off, kWave);
+      if (lane >= off) incl += u;
     }
-    for (int m = 1; m < kWave; m <<= 1) t = max(t, __shfl_xor(t, m, kWave));
-    jmax = max(jmax, t);
-  }
-  for (int j = jmax - 1; j >= 0; --j) {
-    for (int d0 = 0; d0 < num_docs; d0 += kWave) {
-      const int d = d0 + lane;
-      int t = 0;
-      if (d0 < kCached * kWave) {
-#pragma unroll
-        for (int c = 0; c < kCached; ++c)
-          if (d0 == 64 * c) t = tcount[c];
-      } else if (d < num_docs) {
-        t = ceil_div_qt(cu[d + 1] - cu[d], QT, qt_shift);
-      }
-      const uint64_t mask = __ballot(t > j);
-      const int cnt = __popcll(mask);
-      if (tile < cnt) {
-        uint64_t m = mask;  // position of the tile-th set bit
-        for (int k = 0; k < tile; ++k) m &= m - 1;
-        const int dd = d0 + __builtin_ctzll(m);
-        out.doc_start = cu[dd];
-        out.q_lo = cu[dd] + j * QT;
-        out.q_hi = min(cu[dd + 1], out.q_lo + QT);
-        return true;
-      }
-      tile -= cnt;
+    const uint64_t hit = __ballot(base + incl > tile);
+    if (hit) {
+      const int j = __builtin_ctzll(hit);
+      const int dd = d0 + j;
+      const int end = base + __shfl(incl, j, kWave);
+      const int qt = end - 1 - tile;  // query tile inside the document, last first
+      out.doc_start = cu[dd];
+      out.q_lo = cu[dd] + qt * QT;
+      out.q_hi = min(cu[dd + 1], out.q_lo + QT);
+      return true;
     }
+    base += __shfl(incl, kWave - 1, kWave);
   }
   return false;
 }
