@@ -1,10 +1,11 @@
 """Benchmark of the paged-KV attention hot path on one MI355X.
 
 A step is one pass of the hot path over one batch of synthetic input:
-  decode:  paged_kv_append of one new token per live sequence, then
-           paged_decode_attn over the bucketed B=64 batch (50 live rows,
-           14 padding rows in slot 0, contexts 512..1024, sequential pages,
-           H_q=32, H_kv=8, D=128, page_size=128);
+  decode:  the append of one new token per live sequence and the decode
+           over the bucketed B=64 batch (50 live rows, 14 padding rows in
+           slot 0, contexts 512..1024, sequential pages, H_q=32, H_kv=8,
+           D=128, page_size=128), as one paged_decode_attn_append launch
+           (--separate: paged_kv_append, then paged_decode_attn);
   prefill: paged_kv_append of the packed prompts' K/V into shuffled pages,
            then packed_prefill_attn (64 prompts of 64..512 tokens, L ~ 18k).
 
@@ -56,6 +57,9 @@ def parse():
                     help="decode split count: 0 = automatic, 1 = single pass, >1 = per-row splits")
     ap.add_argument("--flags", type=int, default=0,
                     help="decode PKV_F_* flags (4 = balanced schedule, with --num-splits 0)")
+    ap.add_argument("--separate", action="store_true",
+                    help="decode step as paged_kv_append + paged_decode_attn instead of the fused "
+                         "paged_decode_attn_append")
     ap.add_argument("--eager", action="store_true",
                     help="launch every timed call from Python instead of replaying a HIP graph")
     ap.add_argument("--flush", action="store_true",
@@ -141,6 +145,10 @@ def main():
     d_pt, d_bi, d_kl = dev_i32(c.page_table), dev_i32(c.batch_idx), dev_i32(c.kv_len)
     d_abi, d_apos = dev_i32(app_bi), dev_i32(app_pos)
     d_ak, d_av = dev_bf16(app_k), dev_bf16(app_v)
+    row_k = np.zeros((c.B, c.H_kv, c.D), np.uint16)   # the same tokens, indexed by row
+    row_v = np.zeros_like(row_k)
+    row_k[act], row_v[act] = app_k, app_v
+    d_rk, d_rv = dev_bf16(row_k), dev_bf16(row_v)
     max_kv = int(c.kv_len.max())
     balanced = bool(args.flags & pkv.PKV_F_BALANCED)
     S = args.num_splits or (0 if balanced else pkv.paged_decode_num_splits(c.B, c.H_kv, max_kv))
@@ -156,10 +164,18 @@ def main():
                               page_size=c.page_size, scale=float(c.scale), max_kv_len=max_kv,
                               num_splits=S, flags=args.flags, workspace=d_ws, out=d_out, lse=d_lse)
 
-    def decode_step(i):
+    def decode_step_separate(i):
         pkv.paged_kv_append(d_k[i % NL], d_v[i % NL], d_pt, d_abi, d_apos, d_ak, d_av,
                             page_size=c.page_size)
         decode_only(i)
+
+    def decode_step_fused(i):
+        pkv.paged_decode_attn_append(d_q, d_rk, d_rv, d_k[i % NL], d_v[i % NL], d_pt, d_bi, d_kl,
+                                     page_size=c.page_size, scale=float(c.scale),
+                                     max_kv_len=max_kv, num_splits=S, flags=args.flags,
+                                     workspace=d_ws, out=d_out, lse=d_lse)
+
+    decode_step = decode_step_separate if args.separate else decode_step_fused
 
     # ---------------- prefill inputs (packed 64 prompts), one input set per layer
     prefill = None
@@ -256,6 +272,7 @@ def main():
     wall = time.perf_counter() - t0
     # the dominant kernels alone (roofline): decode attention, prefill attention
     dk_total = timed(decode_only, K)
+    alt_total = timed(decode_step_fused if args.separate else decode_step_separate, K)
     pa_total = timed(prefill["attn"], K) if prefill else 0.0
 
     dec_ms, dk_ms = dec_total / K, dk_total / K
@@ -284,6 +301,9 @@ def main():
             "global_batch": int(c.B),
             "kv_bytes_per_step": int(kv_bytes),
             "decode_step_ms": round(dec_ms, 5),
+            "decode_step": ("paged_kv_append + paged_decode_attn" if args.separate else
+                            "paged_decode_attn_append (append and decode fused in one launch)"),
+            ("fused_step_ms" if args.separate else "separate_step_ms"): round(alt_total / K, 5),
             "schedule": (f"balanced: {W} workgroups per KV head" if balanced else
                          f"per-row: {S} split(s) per row"),
             "launch": "eager stream launches" if (args.eager or args.flush) else

@@ -164,6 +164,37 @@ int paged_decode_attn(const void *q, const void *k_pool, const void *v_pool, int
                       float *lse, void *stream);
 
 /*
+ * paged_decode_attn_append - paged_kv_append of each row's new token
+ * followed by paged_decode_attn, in one launch.
+ *
+ * The decode step of the attention forward on the qwen3_flex_inference.py
+ * page updates the cache with the step's token, then attends over the cache
+ * including it.  Here row r's new token, at logical position kv_len[r] - 1,
+ * is k_new[r] / v_new[r] (bf16 [batch][num_kv_heads][head_dim]); kv_len
+ * counts it.  The workgroup that owns that key attends to it straight from
+ * k_new / v_new and writes it into its page, so no key is read back from the
+ * pool in the same launch.  Equivalent to
+ *     paged_kv_append(tokens = live rows, input_pos = kv_len - 1) ;
+ *     paged_decode_attn(same arguments)
+ * with these exact rules: padding rows (slot 0, kv_len <= 0) write nothing
+ * and return (+0, -inf); a row whose kv_len exceeds max_blocks*page_size has
+ * no new token in range, so nothing is written and the row attends to its
+ * first max_blocks*page_size keys; the write is skipped (the token still
+ * attended) when the token's block maps to page 0 or to no page of the pool.
+ * The pool bytes written are bit-exact copies of k_new / v_new.  Other
+ * arguments, the schedule and the workspace are as in paged_decode_attn;
+ * k_pool and v_pool are written.
+ */
+int paged_decode_attn_append(const void *q, const void *k_new, const void *v_new, void *k_pool,
+                             void *v_pool, int32_t num_pages, int32_t page_size,
+                             int32_t num_kv_heads, int32_t head_dim, const int32_t *page_table,
+                             int32_t num_slots, int32_t max_blocks, const int32_t *batch_idx,
+                             const int32_t *kv_len, int32_t batch, int32_t num_q_heads,
+                             float scale, int32_t max_kv_len, int32_t num_splits, uint32_t flags,
+                             void *workspace, size_t workspace_bytes, void *out, float *lse,
+                             void *stream);
+
+/*
  * packed_prefill_attn - document-causal attention over packed prompts.
  *
  * Defined by the prefill of the qwen3_flex_inference.py page: prompts are

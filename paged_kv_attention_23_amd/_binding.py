@@ -67,6 +67,10 @@ def load_library(path: str = LIB_PATH):
                                     _I32, _I32, ctypes.c_float, _I32, _I32, ctypes.c_uint32, _P,
                                     ctypes.c_size_t, _P, _P, _P]
     L.paged_decode_attn.restype = ctypes.c_int
+    L.paged_decode_attn_append.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _I32,
+                                           _I32, _P, _P, _I32, _I32, ctypes.c_float, _I32, _I32,
+                                           ctypes.c_uint32, _P, ctypes.c_size_t, _P, _P, _P]
+    L.paged_decode_attn_append.restype = ctypes.c_int
     L.packed_prefill_attn.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                       ctypes.c_float, _P, _P, _P]
     L.packed_prefill_attn.restype = ctypes.c_int
@@ -182,6 +186,46 @@ def paged_decode_attn(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tenso
                              _dev(out, "out", torch.bfloat16, 3), _dev(lse, "lse", torch.float32, 2),
                              _stream(stream))
     _check(rc, "paged_decode_attn")
+    return out, lse
+
+
+def paged_decode_attn_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                             k_pool: torch.Tensor, v_pool: torch.Tensor, page_table: torch.Tensor,
+                             batch_idx: torch.Tensor, kv_len: torch.Tensor, page_size: int,
+                             scale: float, max_kv_len: int = 0, num_splits: int = 0, flags: int = 0,
+                             workspace: Optional[torch.Tensor] = None,
+                             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                             stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Append each row's new token (k_new/v_new [B, H_kv, D], position kv_len-1) and decode,
+    in one launch; returns (out, lse) as paged_decode_attn."""
+    L = load_library()
+    B, H_q, D = q.shape
+    H_kv, rows, D2 = k_pool.shape
+    if D2 != D or v_pool.shape != k_pool.shape or rows % page_size:
+        raise ValueError("pool shape does not match q / page_size")
+    if tuple(k_new.shape) != (B, H_kv, D) or tuple(v_new.shape) != (B, H_kv, D):
+        raise ValueError("k_new/v_new must be [B, H_kv, D]")
+    num_slots, max_blocks = page_table.shape
+    if batch_idx.shape[0] != B or kv_len.shape[0] != B:
+        raise ValueError("batch_idx and kv_len must have one entry per row")
+    S = int(num_splits)
+    need = paged_decode_workspace_size(B, H_q, H_kv, D, S, int(flags))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr, ws_bytes = (0, 0) if workspace is None else (workspace.data_ptr(), workspace.numel())
+    if out is None:
+        out = torch.empty((B, H_q, D), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H_q), dtype=torch.float32, device=q.device)
+    rc = L.paged_decode_attn_append(
+        _dev(q, "q", torch.bfloat16, 3), _dev(k_new, "k_new", torch.bfloat16, 3),
+        _dev(v_new, "v_new", torch.bfloat16, 3), _dev(k_pool, "k_pool", torch.bfloat16, 3),
+        _dev(v_pool, "v_pool", torch.bfloat16, 3), rows // page_size, page_size, H_kv, D,
+        _dev(page_table, "page_table", torch.int32, 2), num_slots, max_blocks,
+        _dev(batch_idx, "batch_idx", torch.int32, 1), _dev(kv_len, "kv_len", torch.int32, 1), B,
+        H_q, float(scale), int(max_kv_len), S, int(flags), ws_ptr, ws_bytes,
+        _dev(out, "out", torch.bfloat16, 3), _dev(lse, "lse", torch.float32, 2), _stream(stream))
+    _check(rc, "paged_decode_attn_append")
     return out, lse
 
 

@@ -254,12 +254,16 @@ __device__ void write_empty(const PieceOut &dst, int G, int D) {
 
 // Attention of the G query heads of KV head g in row r over the row's keys
 // [lo, hi) (0 <= lo < hi <= n), all four waves of the workgroup together.
-// s is the row's slot (valid).  Ends with a workgroup barrier, so the caller
-// may start another piece right away.
-template <int D>
+// s is the row's slot (valid).  With with_new (fused append, hi == n), key
+// n-1 is the caller's new token: it is attended from k_new/v_new rather than
+// the pool, and written into its page.  Ends with a workgroup barrier, so the
+// caller may start another piece right away.
+template <int D, bool kFused, bool kEarlyNew>
 __device__ void decode_piece(const DecodeArgs &a, char *smem, int r, int g, int s, int lo, int hi,
-                             const PieceOut &dst, int lane, int wave) {
+                             bool with_new, const PieceOut &dst, int lane, int wave) {
+  if constexpr (!kFused) with_new = false;
   using Gm = DecGeom<D>;
+  constexpr int NT = Gm::kDBlocks;
   const int hl = lane & 15, lg = lane >> 4;
   const int G = a.G;
 
@@ -275,6 +279,64 @@ __device__ void decode_piece(const DecodeArgs &a, char *smem, int r, int g, int 
     }
   }
 
+  // New token: K in the Q operand layout (dims 8*lg + 32*ch), V in the
+  // accumulator layout (dims NT*4*lg .. NT*4*lg + D/4 - 1).  With kEarlyNew
+  // they are loaded before the key loop (their latency hides behind it, at
+  // the cost of registers held through it); otherwise after it.
+  u32x4 kq[D / 32], vq[D / 32];
+  int new_page = 0;
+  auto load_new = [&]() {
+    const int64_t nrow = ((int64_t)r * a.H_kv + g) * D;
+#pragma unroll
+    for (int ch = 0; ch < D / 32; ++ch) {
+      kq[ch] = *reinterpret_cast<const u32x4 *>(a.k_new + nrow + 8 * lg + 32 * ch);
+      vq[ch] = *reinterpret_cast<const u32x4 *>(a.v_new + nrow + NT * 4 * lg + 8 * ch);
+    }
+    new_page = a.page_table[(int64_t)s * a.max_blocks + (hi >> a.page_shift)];
+  };
+  // Wave 0's lanes of column 0 write the new K and V rows into their page
+  // where paged_kv_append would (a mapped page of this pool).
+  auto write_new = [&]() {
+    if (hl == 0 && new_page > 0 && new_page < a.num_pages) {
+      const int64_t prow = (int64_t)g * a.plane_rows + ((int64_t)new_page << a.page_shift) +
+                           (hi & ((1 << a.page_shift) - 1));  // hi = n - 1 by then
+#pragma unroll
+      for (int ch = 0; ch < D / 32; ++ch) {
+        *reinterpret_cast<u32x4 *>(a.k_pool_w + prow * D + 8 * lg + 32 * ch) = kq[ch];
+        *reinterpret_cast<u32x4 *>(a.v_pool_w + prow * D + NT * 4 * lg + 8 * ch) = vq[ch];
+      }
+    }
+  };
+  // Score of the new token for head hl, base 2: q . k_new from the Q operand
+  // registers (fp32 products of bf16 values), summed over the lg lanes.
+  auto new_score = [&]() {
+    float dot = 0.f;
+#pragma unroll
+    for (int ch = 0; ch < D / 32; ++ch) {
+      const u32x4 qw = __builtin_bit_cast(u32x4, qop[ch]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        dot = fmaf(bf16_lo(qw[j]), bf16_lo(kq[ch][j]), dot);
+        dot = fmaf(bf16_hi(qw[j]), bf16_hi(kq[ch][j]), dot);
+      }
+    }
+    dot = sum_xor16(dot);
+    dot = sum_xor32(dot);
+    return dot * a.scale_log2;
+  };
+  if (with_new) {
+    hi -= 1;  // the pool supplies keys [lo, n-1); key n-1 is the new token
+    if constexpr (kEarlyNew) {
+      if (wave == 0) load_new();
+    }
+  }
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 o[Gm::kDBlocks];
+#pragma unroll
+  for (int t = 0; t < Gm::kDBlocks; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (lo < hi) {
   // Where this piece's keys live; detect consecutive page ids (one wave vote).
   RowCtx c;
   c.pt_row = a.page_table + (int64_t)s * a.max_blocks;
@@ -303,11 +365,6 @@ __device__ void decode_piece(const DecodeArgs &a, char *smem, int r, int g, int 
 
   const char *kbase = reinterpret_cast<const char *>(a.k_pool + (int64_t)g * a.plane_rows * D);
   const char *vbase = reinterpret_cast<const char *>(a.v_pool + (int64_t)g * a.plane_rows * D);
-
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 o[Gm::kDBlocks];
-#pragma unroll
-  for (int t = 0; t < Gm::kDBlocks; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   char *vlds = smem + wave * Gm::kVBytes;
 
@@ -344,6 +401,29 @@ __device__ void decode_piece(const DecodeArgs &a, char *smem, int r, int g, int 
       t = tn;
     }
     seg_lo = seg_hi;
+  }
+  }  // lo < hi
+
+  // The new token joins wave 0's running state: score from the Q operand
+  // registers (fp32 products of bf16 values), weight p in fp32; then its
+  // rows are written.
+  if (with_new && wave == 0) {
+    if constexpr (!kEarlyNew) load_new();
+    const float x = new_score();
+    const float m_new = fmaxf(m_run, x);
+    const float alpha = fast_exp2(m_run - m_new);  // 0 while m_run = -inf
+    const float pn = fast_exp2(x - m_new);
+    l_run = l_run * alpha + (lg == 0 ? pn : 0.f);  // l is summed over lg below
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int k = NT * i + t;  // element of this lane's D/4 new-V values
+        const uint32_t w = vq[k >> 3][(k >> 1) & 3];
+        o[t][i] = o[t][i] * alpha + pn * ((k & 1) ? bf16_hi(w) : bf16_lo(w));
+      }
+    m_run = m_new;
+    write_new();
   }
 
   // Combine the 4 waves through LDS (the merge area reuses the V tiles).
@@ -397,18 +477,23 @@ __device__ void decode_piece(const DecodeArgs &a, char *smem, int r, int g, int 
 }
 
 // Valid keys of row r (0 for padding rows: slot 0 / out of range / kv_len <= 0),
-// clamped to the page table's capacity.
-__device__ __forceinline__ int row_keys(const DecodeArgs &a, int r, int &slot) {
+// clamped to the page table's capacity.  has_new: with a fused append, the
+// row's new token (position kv_len - 1) lies inside that capacity.
+__device__ __forceinline__ int row_keys(const DecodeArgs &a, int r, int &slot, bool &has_new) {
   const int s = a.batch_idx[r];
-  const int n = min(a.kv_len[r], a.max_blocks << a.page_shift);
+  const int raw = a.kv_len[r];
+  const int cap = a.max_blocks << a.page_shift;
+  const int n = min(raw, cap);
   slot = s;
-  return (s <= 0 || s >= a.num_slots || n <= 0) ? 0 : n;
+  const bool live = !(s <= 0 || s >= a.num_slots || n <= 0);
+  has_new = live && a.k_new != nullptr && raw <= cap;
+  return live ? n : 0;
 }
 
 // Per-row schedule: blockIdx.x enumerates (split, KV head, row), split
 // fastest; split sp of a row covers an equal share of its keys in whole
 // 32-key tiles.  With one split the result is final, else a partial.
-template <int D>
+template <int D, bool kFused>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_rows_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[DecGeom<D>::kSmemBytes];
@@ -420,7 +505,8 @@ void decode_rows_kernel(DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
 
   int s;
-  const int n = row_keys(a, r, s);
+  bool has_new;
+  const int n = row_keys(a, r, s, has_new);
   const int chunk = ((n + S - 1) / S + kTileKeys - 1) & ~(kTileKeys - 1);
   const int64_t lo64 = (int64_t)sp * chunk;
   const int lo = (int)min(lo64, (int64_t)n);
@@ -434,7 +520,8 @@ void decode_rows_kernel(DecodeArgs a) {
     write_empty(dst, a.G, D);
     return;
   }
-  decode_piece<D>(a, smem, r, g, s, lo, hi, dst, lane, wave);
+  const bool with_new = has_new && hi == n;
+  decode_piece<D, kFused, true>(a, smem, r, g, s, lo, hi, with_new, dst, lane, wave);
 }
 
 __device__ __forceinline__ int64_t readlane64(int64_t v, int l) {
@@ -473,7 +560,7 @@ __device__ __forceinline__ int64_t wave_incl_scan64(int64_t v, int lane) {
 // row prefix sums itself (batch_idx / kv_len are a few cached lines), so the
 // plan needs no extra launch.  Everything but the lanes' prefix ends is kept
 // in scalar registers across the pieces.
-template <int D>
+template <int D, bool kFused>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_balanced_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[DecGeom<D>::kSmemBytes];
@@ -489,12 +576,14 @@ void decode_balanced_kernel(DecodeArgs a) {
   int s_first = 0, n_first = 0;
   for (int cb = 0; cb < a.B; cb += kWave) {
     int s = 0, n = 0;
-    if (cb + lane < a.B) n = row_keys(a, cb + lane, s);
+    bool hn = false;
+    if (cb + lane < a.B) n = row_keys(a, cb + lane, s, hn);
+    n |= hn ? 0 : INT32_MIN;  // bit 31: no fused new token for this row
     if (cb == 0) {
       s_first = s;
       n_first = n;
     }
-    TT += wave_sum64((n + kTileKeys - 1) / kTileKeys);
+    TT += wave_sum64(((n & INT32_MAX) + kTileKeys - 1) / kTileKeys);
   }
   const int We = (int)min<int64_t>(W, TT);
   const int last_owner = max(We - 1, 0);
@@ -507,13 +596,15 @@ void decode_balanced_kernel(DecodeArgs a) {
       const int r = cb + lane;
       int s = s_first, n = n_first;
       if (cb != 0) {
+        bool hn = false;
         n = 0;
-        if (r < a.B) n = row_keys(a, r, s);
+        if (r < a.B) n = row_keys(a, r, s, hn);
+        n |= hn ? 0 : INT32_MIN;
       }
       uint64_t mask;
       int64_t pe;  // end of the lane's row in the tile list
       {
-        const int tiles = (n + kTileKeys - 1) / kTileKeys;
+        const int tiles = ((n & INT32_MAX) + kTileKeys - 1) / kTileKeys;
         pe = carry + wave_incl_scan64(tiles, lane);
         const int64_t ps = pe - tiles;
         bool mine = false;
@@ -529,7 +620,9 @@ void decode_balanced_kernel(DecodeArgs a) {
         mask &= mask - 1;
         const int rr = cb + j;
         const int sj = __builtin_amdgcn_readlane(s, j);
-        const int nj = __builtin_amdgcn_readlane(n, j);
+        const int nenc = __builtin_amdgcn_readlane(n, j);
+        const int nj = nenc & INT32_MAX;
+        const bool hnj = nenc >= 0;
         const int64_t ej = readlane64(pe, j);
         const int64_t pj = ej - (nj + kTileKeys - 1) / kTileKeys;
         if (nj == 0) {
@@ -550,7 +643,7 @@ void decode_balanced_kernel(DecodeArgs a) {
             desc_last = (int)((ej * We + TT - 1) / TT) - 1;  // range holding tile ej-1
           }
         }
-        decode_piece<D>(a, smem, rr, g, sj, lo, hi, dst, lane, wave);
+        decode_piece<D, kFused, false>(a, smem, rr, g, sj, lo, hi, hnj && hi == nj, dst, lane, wave);
       }
     }
   }
@@ -651,21 +744,23 @@ __global__ __launch_bounds__(256) void merge_balanced_kernel(DecodeArgs a) {
   }
 }
 
+template <int D, bool kFused>
+static void launch_main(const DecodeArgs &a, dim3 grid, hipStream_t stream) {
+  if (a.balanced)
+    hipLaunchKernelGGL((decode_balanced_kernel<D, kFused>), grid, dim3(kDecThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_rows_kernel<D, kFused>), grid, dim3(kDecThreads), 0, stream, a);
+}
+
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   if (a.B == 0) return hipSuccess;
   const bool balanced = a.balanced != 0;
+  const bool fused = a.k_new != nullptr;
   const dim3 grid((unsigned)((int64_t)a.num_splits * a.H_kv * (balanced ? 1 : a.B)));
-  if (balanced) {
-    if (a.D == 128)
-      hipLaunchKernelGGL(decode_balanced_kernel<128>, grid, dim3(kDecThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL(decode_balanced_kernel<64>, grid, dim3(kDecThreads), 0, stream, a);
-  } else {
-    if (a.D == 128)
-      hipLaunchKernelGGL(decode_rows_kernel<128>, grid, dim3(kDecThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL(decode_rows_kernel<64>, grid, dim3(kDecThreads), 0, stream, a);
-  }
+  if (a.D == 128)
+    fused ? launch_main<128, true>(a, grid, stream) : launch_main<128, false>(a, grid, stream);
+  else
+    fused ? launch_main<64, true>(a, grid, stream) : launch_main<64, false>(a, grid, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_splits == 1) return e;
   if (balanced) {

@@ -179,13 +179,14 @@ int32_t paged_decode_balanced_parts(int32_t batch, int32_t num_kv_heads, int32_t
   return balanced_parts(batch, num_kv_heads, max_kv_len > 0 ? max_kv_len : 1, device_cus());
 }
 
-int paged_decode_attn(const void *q, const void *k_pool, const void *v_pool, int32_t num_pages,
-                      int32_t page_size, int32_t num_kv_heads, int32_t head_dim,
-                      const int32_t *page_table, int32_t num_slots, int32_t max_blocks,
-                      const int32_t *batch_idx, const int32_t *kv_len, int32_t batch,
-                      int32_t num_q_heads, float scale, int32_t max_kv_len, int32_t num_splits,
-                      uint32_t flags, void *workspace, size_t workspace_bytes, void *out,
-                      float *lse, void *stream) {
+static int decode_common(const char *who, const void *q, const void *k_new, const void *v_new,
+                         const void *k_pool, const void *v_pool, bool fused, int32_t num_pages,
+                         int32_t page_size, int32_t num_kv_heads, int32_t head_dim,
+                         const int32_t *page_table, int32_t num_slots, int32_t max_blocks,
+                         const int32_t *batch_idx, const int32_t *kv_len, int32_t batch,
+                         int32_t num_q_heads, float scale, int32_t max_kv_len, int32_t num_splits,
+                         uint32_t flags, void *workspace, size_t workspace_bytes, void *out,
+                         float *lse, void *stream) {
   if (batch < 0) return fail(PKV_E_SHAPE, "batch must be >= 0 (got %d)", batch);
   int rc = check_pool(num_pages, page_size, num_kv_heads, head_dim, num_slots, max_blocks);
   if (rc) return rc;
@@ -203,12 +204,14 @@ int paged_decode_attn(const void *q, const void *k_pool, const void *v_pool, int
   if ((int64_t)batch * num_kv_heads * PKV_MAX_SPLITS > INT32_MAX)
     return fail(PKV_E_SHAPE, "batch*num_kv_heads too large (got %d*%d)", batch, num_kv_heads);
   if (batch == 0) return PKV_OK;
-  if (!q || !k_pool || !v_pool || !page_table || !batch_idx || !kv_len || !out || !lse)
-    return fail(PKV_E_NULL, "paged_decode_attn: a required pointer is NULL");
-  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
-    return fail(PKV_E_ALIGN, "paged_decode_attn: bf16 tensors must be 16-byte aligned");
+  if (!q || !k_pool || !v_pool || !page_table || !batch_idx || !kv_len || !out || !lse ||
+      (fused && (!k_new || !v_new)))
+    return fail(PKV_E_NULL, "%s: a required pointer is NULL", who);
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out) ||
+      (fused && (!aligned16(k_new) || !aligned16(v_new))))
+    return fail(PKV_E_ALIGN, "%s: bf16 tensors must be 16-byte aligned", who);
   if (!aligned4(page_table) || !aligned4(batch_idx) || !aligned4(kv_len) || !aligned4(lse))
-    return fail(PKV_E_ALIGN, "paged_decode_attn: int32/fp32 tensors must be 4-byte aligned");
+    return fail(PKV_E_ALIGN, "%s: int32/fp32 tensors must be 4-byte aligned", who);
 
   const int32_t cap = max_blocks * page_size;
   const int32_t kv_bound = (max_kv_len <= 0 || max_kv_len > cap) ? cap : max_kv_len;
@@ -234,11 +237,11 @@ int paged_decode_attn(const void *q, const void *k_pool, const void *v_pool, int
     const size_t need = paged_decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim,
                                                     balanced ? 0 : S, flags);
     if (!workspace || workspace_bytes < need)
-      return fail(PKV_E_WORKSPACE, "paged_decode_attn: %s needs %zu workspace bytes (got %zu%s)",
+      return fail(PKV_E_WORKSPACE, "%s: %s needs %zu workspace bytes (got %zu%s)", who,
                   balanced ? "the balanced schedule" : "this split count", need, workspace_bytes,
                   workspace ? "" : ", NULL");
     if (!aligned16(workspace))
-      return fail(PKV_E_ALIGN, "paged_decode_attn: workspace must be 16-byte aligned");
+      return fail(PKV_E_ALIGN, "%s: workspace must be 16-byte aligned", who);
     char *ws = (char *)workspace;
     if (balanced) {
       const size_t rows = (size_t)num_kv_heads *
@@ -275,7 +278,38 @@ int paged_decode_attn(const void *q, const void *k_pool, const void *v_pool, int
   a.contig_mode = (flags & PKV_F_NO_CONTIG_DETECT) ? 2 : (flags & PKV_F_ASSUME_CONTIGUOUS) ? 1 : 0;
   a.out = (uint16_t *)out;
   a.lse = lse;
-  return launch_status(pkv::launch_decode(a, (hipStream_t)stream), "paged_decode_attn launch");
+  a.k_new = fused ? (const uint16_t *)k_new : nullptr;
+  a.v_new = fused ? (const uint16_t *)v_new : nullptr;
+  a.k_pool_w = fused ? (uint16_t *)k_pool : nullptr;
+  a.v_pool_w = fused ? (uint16_t *)v_pool : nullptr;
+  return launch_status(pkv::launch_decode(a, (hipStream_t)stream), who);
+}
+
+int paged_decode_attn(const void *q, const void *k_pool, const void *v_pool, int32_t num_pages,
+                      int32_t page_size, int32_t num_kv_heads, int32_t head_dim,
+                      const int32_t *page_table, int32_t num_slots, int32_t max_blocks,
+                      const int32_t *batch_idx, const int32_t *kv_len, int32_t batch,
+                      int32_t num_q_heads, float scale, int32_t max_kv_len, int32_t num_splits,
+                      uint32_t flags, void *workspace, size_t workspace_bytes, void *out,
+                      float *lse, void *stream) {
+  return decode_common("paged_decode_attn", q, nullptr, nullptr, k_pool, v_pool, false, num_pages,
+                       page_size, num_kv_heads, head_dim, page_table, num_slots, max_blocks,
+                       batch_idx, kv_len, batch, num_q_heads, scale, max_kv_len, num_splits, flags,
+                       workspace, workspace_bytes, out, lse, stream);
+}
+
+int paged_decode_attn_append(const void *q, const void *k_new, const void *v_new, void *k_pool,
+                             void *v_pool, int32_t num_pages, int32_t page_size,
+                             int32_t num_kv_heads, int32_t head_dim, const int32_t *page_table,
+                             int32_t num_slots, int32_t max_blocks, const int32_t *batch_idx,
+                             const int32_t *kv_len, int32_t batch, int32_t num_q_heads,
+                             float scale, int32_t max_kv_len, int32_t num_splits, uint32_t flags,
+                             void *workspace, size_t workspace_bytes, void *out, float *lse,
+                             void *stream) {
+  return decode_common("paged_decode_attn_append", q, k_new, v_new, k_pool, v_pool, true,
+                       num_pages, page_size, num_kv_heads, head_dim, page_table, num_slots,
+                       max_blocks, batch_idx, kv_len, batch, num_q_heads, scale, max_kv_len,
+                       num_splits, flags, workspace, workspace_bytes, out, lse, stream);
 }
 
 int packed_prefill_attn(const void *q, const void *k, const void *v, const int32_t *cu_seqlens,

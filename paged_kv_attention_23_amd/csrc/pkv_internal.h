@@ -34,6 +34,11 @@ struct DecodeArgs {
   int4 *desc;
   uint16_t *out;                   // [B][H_q][D] bf16
   float *lse;                      // [B][H_q]
+  // Fused append (paged_decode_attn_append): each live row's new token, at
+  // position kv_len - 1, comes from k_new/v_new [B][H_kv][D] and is written
+  // into the pools through k_pool_w/v_pool_w.  All NULL for plain decode.
+  const uint16_t *k_new, *v_new;
+  uint16_t *k_pool_w, *v_pool_w;
 };
 
 struct PrefillArgs {

@@ -1,0 +1,154 @@
+"""GPU parity of paged_decode_attn_append (append + decode in one launch) against the
+float64 oracle: the oracle appends each row's token with its scatter, then decodes."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import BF16_NAN, make_case, make_decode_case
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - GPU tests only run on the GPU machine
+    pytest.skip("no GPU", allow_module_level=True)
+
+import paged_kv_attention_23_amd as pkv  # noqa: E402
+from gpu_util import check_close, dev_bf16, dev_i32, host_bits  # noqa: E402
+
+MODES = {"detect": 0, "walk": pkv.PKV_F_NO_CONTIG_DETECT}
+
+
+def _sched(splits):
+    return (0, pkv.PKV_F_BALANCED) if splits == "balanced" else (splits, 0)
+
+
+def _row_tokens(c):
+    """The case's append tokens, indexed by row ([B, H_kv, D]; zero for padding rows)."""
+    kn = np.zeros((c.B, c.H_kv, c.D), np.uint16)
+    vn = np.zeros_like(kn)
+    act = c.active_rows()
+    kn[act] = c.app_k
+    vn[act] = c.app_v
+    return kn, vn
+
+
+def _expected(c):
+    kp, vp = oracle.append_pages(c.k_pool, c.v_pool, c.num_pages, c.page_size, c.page_table,
+                                 c.app_batch_idx, c.app_input_pos, c.app_k, c.app_v)
+    out, lse = oracle.decode_case(c, kp, vp)
+    return kp, vp, out, lse
+
+
+def _run_fused(c, kn, vn, splits, flags, max_kv_len=None, kv_len=None):
+    S, extra = _sched(splits)
+    kd, vd = dev_bf16(c.k_pool), dev_bf16(c.v_pool)
+    kl = c.kv_len if kv_len is None else kv_len
+    out, lse = pkv.paged_decode_attn_append(
+        dev_bf16(c.q), dev_bf16(kn), dev_bf16(vn), kd, vd, dev_i32(c.page_table),
+        dev_i32(c.batch_idx), dev_i32(kl), page_size=c.page_size, scale=float(c.scale),
+        max_kv_len=int(kl.max()) if max_kv_len is None else max_kv_len, num_splits=S,
+        flags=flags | extra)
+    torch.cuda.synchronize()
+    return out, lse, host_bits(kd), host_bits(vd)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 0, "balanced"])
+@pytest.mark.parametrize("mode", list(MODES))
+def test_fused_qwen3_b8(splits, mode):
+    """The B=8 Qwen3-shaped step: pools bit-exact, outputs within tolerance."""
+    print(f"fused cfg2 splits={splits} mode={mode}", flush=True)
+    c = make_case(2, fill="nan")
+    kp, vp, out_ref, lse_ref = _expected(c)
+    kn, vn = _row_tokens(c)
+    out, lse, kb, vb = _run_fused(c, kn, vn, splits, MODES[mode])
+    check_close(out, lse, out_ref, lse_ref, f"fused cfg2 S{splits} {mode}")
+    assert np.array_equal(kb, kp) and np.array_equal(vb, vp)
+
+
+SMALL = [
+    # (seed, H_q, H_kv, D, ps, lens, slots)
+    (61, 8, 8, 128, 16, [1, 15, 16, 17, 31, 32, 33, 200], None),        # G = 1, one-key rows
+    (62, 16, 2, 128, 32, [1, 63, 64, 65, 500], None),                   # G = 8
+    (63, 16, 1, 64, 64, [1, 2, 127, 128, 129, 640], None),              # G = 16, D = 64
+    (64, 32, 8, 128, 16, [16 * 40, 16 * 70 + 3, 33], None),             # > 64 blocks
+    (65, 32, 8, 128, 128, [700, 1, 0, 513] * 4,
+     [0 if i % 4 == 1 else i + 1 for i in range(16)]),                  # padding rows
+]
+
+
+def _small(seed, H_q, H_kv, D, ps, lens, slots):
+    B = len(lens)
+    slots = slots if slots is not None else list(range(1, B + 1))
+    need = sum(-(-n // ps) for n, s in zip(lens, slots) if s)
+    mb = max([-(-n // ps) for n in lens] + [1])
+    return make_decode_case(name="fused", seed=seed, H_q=H_q, H_kv=H_kv, D=D, page_size=ps,
+                            num_pages=need + 3, num_slots=max(slots) + 1, max_blocks=mb,
+                            row_slots=slots, row_lens=lens, layout="shuffled", fill="nan",
+                            append_last=True)
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=[f"seed{s[0]}" for s in SMALL])
+@pytest.mark.parametrize("splits", [1, 2, 5, 0, "balanced"])
+def test_fused_edge_shapes(spec, splits):
+    print(f"fused small seed={spec[0]} splits={splits}", flush=True)
+    c = _small(*spec)
+    kp, vp, out_ref, lse_ref = _expected(c)
+    kn, vn = _row_tokens(c)
+    for mode in MODES.values():
+        out, lse, kb, vb = _run_fused(c, kn, vn, splits, mode)
+        check_close(out, lse, out_ref, lse_ref, f"fused seed{spec[0]} S{splits} flags{mode}")
+        assert np.array_equal(kb, kp) and np.array_equal(vb, vp)
+
+
+def test_fused_unmapped_block_and_overlong_row():
+    """Row 0's new token sits alone in a block that maps to page 0: it is attended but not
+    written.  Row 1's kv_len exceeds the table: no new token, the row sees its first
+    max_blocks*page_size keys and nothing is written."""
+    print("fused unmapped / overlong", flush=True)
+    ps = 16
+    c = make_decode_case(name="fused-edge", seed=66, H_q=8, H_kv=2, D=128, page_size=ps,
+                         num_pages=16, num_slots=3, max_blocks=4, row_slots=[1, 2],
+                         row_lens=[32, 64], layout="shuffled", fill="zero")
+    rng = np.random.default_rng(66)
+    kn = (rng.integers(0, 1 << 16, size=(2, c.H_kv, c.D)) & 0x3FFF).astype(np.uint16)  # finite bf16
+    vn = (rng.integers(0, 1 << 16, size=(2, c.H_kv, c.D)) & 0x3FFF).astype(np.uint16)
+    kv_len = np.array([33, 64 + 7], np.int32)  # row 0: new token at 32 (block 2, unmapped)
+    assert c.page_table[1, 2] == 0
+    used = set(c.page_table[1:].ravel().tolist())
+    spare = next(p for p in range(1, c.num_pages) if p not in used)
+    # expectation: block 2 of row 0 mapped to a spare page that holds the new token
+    pt_ref = c.page_table.copy()
+    pt_ref[1, 2] = spare
+    kp_ref, vp_ref = c.k_pool.copy(), c.v_pool.copy()
+    kp_ref[:, spare * ps] = kn[0]
+    vp_ref[:, spare * ps] = vn[0]
+    cap = c.max_blocks * ps
+    out_ref, lse_ref = oracle.decode(c.q, kp_ref, vp_ref, c.num_pages, ps, pt_ref, c.batch_idx,
+                                     np.zeros(2, np.int32), np.minimum(kv_len, cap), c.scale)
+    for splits in (1, 2, 0, "balanced"):
+        out, lse, kb, vb = _run_fused(c, kn, vn, splits, 0, max_kv_len=0, kv_len=kv_len)
+        check_close(out, lse, out_ref, lse_ref, f"fused edge S{splits}")
+        assert np.array_equal(kb, c.k_pool) and np.array_equal(vb, c.v_pool)  # nothing written
+
+
+def test_fused_matches_separate_calls():
+    """Fused = paged_kv_append then paged_decode_attn on the GPU (same schedule)."""
+    print("fused vs separate", flush=True)
+    c = make_case(2, fill="nan")
+    kn, vn = _row_tokens(c)
+    out_f, lse_f, kb, vb = _run_fused(c, kn, vn, 1, 0)
+    kd, vd = dev_bf16(c.k_pool), dev_bf16(c.v_pool)
+    pt, bi, kl = dev_i32(c.page_table), dev_i32(c.batch_idx), dev_i32(c.kv_len)
+    pkv.paged_kv_append(kd, vd, pt, dev_i32(c.app_batch_idx), dev_i32(c.app_input_pos),
+                        dev_bf16(c.app_k), dev_bf16(c.app_v), page_size=c.page_size)
+    out_s, lse_s = pkv.paged_decode_attn(dev_bf16(c.q), kd, vd, pt, bi, kl, page_size=c.page_size,
+                                         scale=float(c.scale), max_kv_len=int(c.kv_len.max()),
+                                         num_splits=1)
+    torch.cuda.synchronize()
+    assert np.array_equal(kb, host_bits(kd)) and np.array_equal(vb, host_bits(vd))
+    o1 = out_f.float().cpu().numpy()
+    o2 = out_s.float().cpu().numpy()
+    assert np.abs(o1 - o2).max() <= 1.6e-2
+    assert np.abs(lse_f.cpu().numpy() - lse_s.cpu().numpy()).max() <= 1e-3

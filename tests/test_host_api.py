@@ -32,6 +32,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _declared()
     assert set(names) >= {"paged_kv_append", "paged_decode_attn", "packed_prefill_attn",
+                          "paged_decode_attn_append",
                           "paged_decode_workspace_size", "paged_decode_num_splits",
                           "paged_decode_balanced_parts",
                           "pkv_last_error"}
@@ -91,6 +92,35 @@ def test_decode_rejects(lib, kw, code, msg):
     rc = _decode(lib, **kw)
     assert rc == code, (rc, B.last_error())
     assert msg in B.last_error()
+
+
+def _fused(lib, **kw):
+    a = dict(q=FAKE, kn=FAKE, vn=FAKE, k=FAKE, v=FAKE, num_pages=8, page_size=16, H_kv=2, D=128,
+             pt=FAKE, num_slots=3, max_blocks=4, bi=FAKE, kl=FAKE, batch=2, H_q=4, scale=0.125,
+             max_kv_len=64, splits=1, flags=0, ws=0, ws_bytes=0, out=FAKE, lse=FAKE, stream=0)
+    a.update(kw)
+    return lib.paged_decode_attn_append(a["q"], a["kn"], a["vn"], a["k"], a["v"], a["num_pages"],
+                                        a["page_size"], a["H_kv"], a["D"], a["pt"],
+                                        a["num_slots"], a["max_blocks"], a["bi"], a["kl"],
+                                        a["batch"], a["H_q"], a["scale"], a["max_kv_len"],
+                                        a["splits"], a["flags"], a["ws"], a["ws_bytes"], a["out"],
+                                        a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(kn=0), -1, "NULL"),
+    (dict(vn=0), -1, "NULL"),
+    (dict(kn=FAKE + 2), -3, "aligned"),
+    (dict(vn=FAKE + 8), -3, "aligned"),
+    (dict(D=96), -2, "head_dim"),
+    (dict(splits=2), -4, "workspace"),
+])
+def test_fused_rejects(lib, kw, code, msg):
+    rc = _fused(lib, **kw)
+    assert rc == code, (rc, B.last_error())
+    assert msg in B.last_error()
+    if code != -2:
+        assert "paged_decode_attn_append" in B.last_error()
 
 
 def test_decode_empty_batch_is_noop(lib):
