@@ -6,8 +6,10 @@ A step is one pass of the hot path over one batch of synthetic input:
            slot 0, contexts 512..1024, sequential pages, H_q=32, H_kv=8,
            D=128, page_size=128), as one paged_decode_attn_append launch
            (--separate: paged_kv_append, then paged_decode_attn);
-  prefill: paged_kv_append of the packed prompts' K/V into shuffled pages,
-           then packed_prefill_attn (64 prompts of 64..512 tokens, L ~ 18k).
+  prefill: the scatter of the packed prompts' K/V into shuffled pages and
+           the document-causal attention (64 prompts of 64..512 tokens,
+           L ~ 18k), as one packed_prefill_attn_append launch (--separate:
+           paged_kv_append, then packed_prefill_attn).
 
 Cold data without a flush: like the layers of a model, the benchmark keeps
 several independent KV caches (and prefill inputs) and runs the steps back to
@@ -58,8 +60,7 @@ def parse():
     ap.add_argument("--flags", type=int, default=0,
                     help="decode PKV_F_* flags (4 = balanced schedule, with --num-splits 0)")
     ap.add_argument("--separate", action="store_true",
-                    help="decode step as paged_kv_append + paged_decode_attn instead of the fused "
-                         "paged_decode_attn_append")
+                    help="steps as paged_kv_append + attention instead of the fused entry points")
     ap.add_argument("--eager", action="store_true",
                     help="launch every timed call from Python instead of replaying a HIP graph")
     ap.add_argument("--flush", action="store_true",
@@ -202,13 +203,23 @@ def main():
             pkv.packed_prefill_attn(p_q[j], p_k[j], p_v[j], p_cu, scale=float(pc.scale),
                                     out=p_out, lse=p_lse)
 
-        def prefill_step(i):
+        p_slots = dev_i32(np.arange(1, pc.n_docs + 1, dtype=np.int32))
+
+        def prefill_step_separate(i):
             j = i % NP
             pkv.paged_kv_append(p_kpool[j], p_vpool[j], p_pt, p_bi, p_ip, p_k[j], p_v[j],
                                 page_size=pc.page_size)
             prefill_attn(i)
 
-        prefill = dict(case=pc, step=prefill_step, attn=prefill_attn, layers=NP)
+        def prefill_step_fused(i):
+            j = i % NP
+            pkv.packed_prefill_attn_append(p_q[j], p_k[j], p_v[j], p_cu, float(pc.scale),
+                                           p_kpool[j], p_vpool[j], p_pt, p_slots, pc.page_size,
+                                           out=p_out, lse=p_lse)
+
+        prefill = dict(case=pc, layers=NP, attn=prefill_attn,
+                       step=prefill_step_separate if args.separate else prefill_step_fused,
+                       alt=prefill_step_fused if args.separate else prefill_step_separate)
 
     flush_buf = torch.ones(1024 * 1024 * 1024 // 4, dtype=torch.float32, device=dev) \
         if args.flush else None
@@ -274,6 +285,7 @@ def main():
     dk_total = timed(decode_only, K)
     alt_total = timed(decode_step_fused if args.separate else decode_step_separate, K)
     pa_total = timed(prefill["attn"], K) if prefill else 0.0
+    palt_total = timed(prefill["alt"], K) if prefill else 0.0
 
     dec_ms, dk_ms = dec_total / K, dk_total / K
     value = kv_bytes / (dec_ms * 1e-3) / 1e9
@@ -336,6 +348,9 @@ def main():
             "flops_per_call": int(flops),
             "attn_us": round(pa_ms * 1e3, 3),
             "step_us": round(pre_ms * 1e3, 3),
+            "step": ("paged_kv_append + packed_prefill_attn" if args.separate else
+                     "packed_prefill_attn_append (scatter and attention fused in one launch)"),
+            ("fused_step_us" if args.separate else "separate_step_us"): round(palt_total / K * 1e3, 3),
             "tflops": round(tflops, 2),
             "roofline": {
                 "bound": "mfma",

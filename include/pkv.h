@@ -220,6 +220,38 @@ int packed_prefill_attn(const void *q, const void *k, const void *v, const int32
                         int32_t num_kv_heads, int32_t head_dim, float scale, void *out,
                         float *lse, void *stream);
 
+/*
+ * packed_prefill_attn_append - packed_prefill_attn plus the scatter of every
+ * document's K/V into its pages, in one launch.
+ *
+ * The prefill of the qwen3_flex_inference.py page fills the paged cache with
+ * the prompts' K/V (the cache update of the attention forward) and attends
+ * over the packed prompts.  Document d (rows [cu_seqlens[d], cu_seqlens[d+1]))
+ * lives in batch slot doc_slots[d], token j of it at logical position j (no
+ * cached prefix).  Equivalent to
+ *     paged_kv_append(k_pool, v_pool, ..., batch_idx = slot of each token,
+ *                     input_pos = position in its document, k, v) ;
+ *     packed_prefill_attn(q, k, v, cu_seqlens, ...)
+ * with paged_kv_append's skip rules (slot 0 or out of range, block past
+ * max_blocks, page 0 or out of range: nothing written for that token).  The
+ * workgroup holding a document's longest key range writes that document's
+ * rows while it streams them through LDS, so the scatter reads no extra HBM.
+ *
+ *   q, k, v, cu_seqlens, out, lse as in packed_prefill_attn
+ *   k_pool, v_pool   bf16 [num_kv_heads][num_pages*page_size][head_dim], written
+ *   page_table       int32 [num_slots][max_blocks]
+ *   doc_slots        int32 [num_docs], device
+ *
+ * Requirements: those of packed_prefill_attn and paged_kv_append.
+ */
+int packed_prefill_attn_append(const void *q, const void *k, const void *v,
+                               const int32_t *cu_seqlens, int32_t num_docs, int32_t total_len,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               float scale, void *out, float *lse, void *k_pool, void *v_pool,
+                               int32_t num_pages, int32_t page_size, const int32_t *page_table,
+                               int32_t num_slots, int32_t max_blocks, const int32_t *doc_slots,
+                               void *stream);
+
 /* Text for the most recent non-zero status returned on this thread. */
 const char *pkv_last_error(void);
 

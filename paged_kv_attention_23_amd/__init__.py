@@ -11,6 +11,9 @@ libpkv.so (include/pkv.h):
                        the two above fused: each row's new token is
                        attended from registers and written into its page
   packed_prefill_attn  document-causal attention over packed prompts
+  packed_prefill_attn_append
+                       the prefill plus the scatter of the prompts' K/V
+                       into their pages, in one launch
 
 This package is the thin Python binding: it marshals torch tensors into the
 C calls and nothing else.
@@ -24,6 +27,7 @@ from ._binding import (  # noqa: F401
     last_error,
     load_library,
     packed_prefill_attn,
+    packed_prefill_attn_append,
     paged_decode_attn,
     paged_decode_attn_append,
     paged_decode_balanced_parts,

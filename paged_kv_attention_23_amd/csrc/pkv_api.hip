@@ -312,13 +312,16 @@ int paged_decode_attn_append(const void *q, const void *k_new, const void *v_new
                        num_splits, flags, workspace, workspace_bytes, out, lse, stream);
 }
 
-int packed_prefill_attn(const void *q, const void *k, const void *v, const int32_t *cu_seqlens,
-                        int32_t num_docs, int32_t total_len, int32_t num_q_heads,
-                        int32_t num_kv_heads, int32_t head_dim, float scale, void *out,
-                        float *lse, void *stream) {
+static int prefill_common(const char *who, const void *q, const void *k, const void *v,
+                          const int32_t *cu_seqlens, int32_t num_docs, int32_t total_len,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float scale,
+                          void *out, float *lse, bool fused, void *k_pool, void *v_pool,
+                          int32_t num_pages, int32_t page_size, const int32_t *page_table,
+                          int32_t num_slots, int32_t max_blocks, const int32_t *doc_slots,
+                          void *stream) {
   if (total_len < 0 || num_docs < 0)
     return fail(PKV_E_SHAPE, "total_len and num_docs must be >= 0 (got %d, %d)", total_len, num_docs);
-  if (head_dim != 128) return fail(PKV_E_SHAPE, "packed_prefill_attn supports head_dim 128 (got %d)", head_dim);
+  if (head_dim != 128) return fail(PKV_E_SHAPE, "%s supports head_dim 128 (got %d)", who, head_dim);
   if (num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
     return fail(PKV_E_SHAPE, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
                 num_q_heads, num_kv_heads);
@@ -326,14 +329,21 @@ int packed_prefill_attn(const void *q, const void *k, const void *v, const int32
     return fail(PKV_E_SHAPE, "at most 16 query heads per KV head are supported (got %d)",
                 num_q_heads / num_kv_heads);
   if (!(scale > 0.f) || isinf(scale)) return fail(PKV_E_SHAPE, "scale must be finite and positive");
+  if (fused) {
+    int rc = check_pool(num_pages, page_size, num_kv_heads, head_dim, num_slots, max_blocks);
+    if (rc) return rc;
+  }
   if (total_len == 0) return PKV_OK;
   if (num_docs == 0) return fail(PKV_E_SHAPE, "total_len > 0 needs at least one document");
-  if (!q || !k || !v || !cu_seqlens || !out || !lse)
-    return fail(PKV_E_NULL, "packed_prefill_attn: a required pointer is NULL");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
-    return fail(PKV_E_ALIGN, "packed_prefill_attn: bf16 tensors must be 16-byte aligned");
-  if (!aligned4(cu_seqlens) || !aligned4(lse))
-    return fail(PKV_E_ALIGN, "packed_prefill_attn: int32/fp32 tensors must be 4-byte aligned");
+  if (!q || !k || !v || !cu_seqlens || !out || !lse ||
+      (fused && (!k_pool || !v_pool || !page_table || !doc_slots)))
+    return fail(PKV_E_NULL, "%s: a required pointer is NULL", who);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      (fused && (!aligned16(k_pool) || !aligned16(v_pool))))
+    return fail(PKV_E_ALIGN, "%s: bf16 tensors must be 16-byte aligned", who);
+  if (!aligned4(cu_seqlens) || !aligned4(lse) ||
+      (fused && (!aligned4(page_table) || !aligned4(doc_slots))))
+    return fail(PKV_E_ALIGN, "%s: int32/fp32 tensors must be 4-byte aligned", who);
   pkv::PrefillArgs a;
   a.q = (const uint16_t *)q;
   a.k = (const uint16_t *)k;
@@ -347,7 +357,37 @@ int packed_prefill_attn(const void *q, const void *k, const void *v, const int32
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.out = (uint16_t *)out;
   a.lse = lse;
-  return launch_status(pkv::launch_prefill(a, 0, (hipStream_t)stream), "packed_prefill_attn launch");
+  a.k_pool = fused ? (uint16_t *)k_pool : nullptr;
+  a.v_pool = fused ? (uint16_t *)v_pool : nullptr;
+  a.page_table = fused ? page_table : nullptr;
+  a.doc_slots = fused ? doc_slots : nullptr;
+  a.plane_rows = fused ? (int64_t)num_pages * page_size : 0;
+  a.num_pages = num_pages;
+  a.page_shift = fused ? log2_exact(page_size) : 0;
+  a.num_slots = num_slots;
+  a.max_blocks = max_blocks;
+  return launch_status(pkv::launch_prefill(a, (hipStream_t)stream), who);
+}
+
+int packed_prefill_attn(const void *q, const void *k, const void *v, const int32_t *cu_seqlens,
+                        int32_t num_docs, int32_t total_len, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim, float scale, void *out,
+                        float *lse, void *stream) {
+  return prefill_common("packed_prefill_attn", q, k, v, cu_seqlens, num_docs, total_len,
+                        num_q_heads, num_kv_heads, head_dim, scale, out, lse, false, nullptr,
+                        nullptr, 0, 0, nullptr, 0, 0, nullptr, stream);
+}
+
+int packed_prefill_attn_append(const void *q, const void *k, const void *v,
+                               const int32_t *cu_seqlens, int32_t num_docs, int32_t total_len,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               float scale, void *out, float *lse, void *k_pool, void *v_pool,
+                               int32_t num_pages, int32_t page_size, const int32_t *page_table,
+                               int32_t num_slots, int32_t max_blocks, const int32_t *doc_slots,
+                               void *stream) {
+  return prefill_common("packed_prefill_attn_append", q, k, v, cu_seqlens, num_docs, total_len,
+                        num_q_heads, num_kv_heads, head_dim, scale, out, lse, true, k_pool, v_pool,
+                        num_pages, page_size, page_table, num_slots, max_blocks, doc_slots, stream);
 }
 
 }  // extern "C"

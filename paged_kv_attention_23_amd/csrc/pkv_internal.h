@@ -49,10 +49,17 @@ struct PrefillArgs {
   float scale_log2;
   uint16_t *out;                   // [L][H_q][D]
   float *lse;                      // [L][H_q]
+  // Fused scatter (packed_prefill_attn_append): token j of document d goes to
+  // slot doc_slots[d], position j of the paged pools.  k_pool NULL: none.
+  uint16_t *k_pool, *v_pool;       // [H_kv][plane_rows][D]
+  const int32_t *page_table;       // [num_slots][max_blocks]
+  const int32_t *doc_slots;        // [num_docs]
+  int64_t plane_rows;
+  int32_t num_pages, page_shift, num_slots, max_blocks;
 };
 
 hipError_t launch_kv_append(const AppendArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
-hipError_t launch_prefill(const PrefillArgs &a, int32_t num_tiles_bound, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 
 }  // namespace pkv

@@ -44,7 +44,7 @@ constexpr int kPfLoads = kPfBN * (2 * kPfD / 16) / kPfThreads;  // 16-byte piece
 constexpr float kLazy = 8.f;                         // lazy-rescale threshold, log2 units
 
 struct PfTile {
-  int doc_start, q_lo, q_hi;
+  int doc, doc_start, doc_end, q_lo, q_hi;
 };
 
 // Tile number -> (document, query tile), document-major: the tiles of
@@ -75,7 +75,9 @@ __device__ bool find_tile(const int32_t *cu, int num_docs, int QT, int qt_shift,
       const int dd = d0 + j;
       const int end = base + __shfl(incl, j, kWave);
       const int qt = end - 1 - tile;  // query tile inside the document, last first
+      out.doc = dd;
       out.doc_start = cu[dd];
+      out.doc_end = cu[dd + 1];
       out.q_lo = cu[dd] + qt * QT;
       out.q_hi = min(cu[dd + 1], out.q_lo + QT);
       return true;
@@ -85,6 +87,7 @@ __device__ bool find_tile(const int32_t *cu, int num_docs, int QT, int qt_shift,
   return false;
 }
 
+template <bool kFused>
 __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kPfSmem];
@@ -101,6 +104,16 @@ void prefill_kernel(PrefillArgs a) {
   PfTile tl;
   if (!find_tile(a.cu_seqlens, a.num_docs, QT, qt_shift, tile, lane, tl)) return;  // uniform
   const int k_lo = tl.doc_start, k_hi = tl.q_hi;
+  // Fused scatter: the document's last query tile reads every key of the
+  // document (its key range ends at the document end), so it alone writes
+  // the document's K/V rows of this head into their pages, from the stage
+  // registers.  Skip rules as in paged_kv_append.
+  int slot = 0;
+  bool scatter = false;
+  if constexpr (kFused) {
+    slot = a.doc_slots[tl.doc];
+    scatter = tl.q_hi == tl.doc_end && slot > 0 && slot < a.num_slots;
+  }
 
   // Rows of this wave: column block qb, column hl -> tile row R.
   int col_head[2], col_q[2];
@@ -128,6 +141,7 @@ void prefill_kernel(PrefillArgs a) {
   const uint16_t *kg = a.k + (int64_t)g * D;
   const uint16_t *vg = a.v + (int64_t)g * D;
   u32x4 stk[kPfLoads], stv[kPfLoads];
+  int spage[kPfLoads];  // fused scatter: page of each piece's key (0 = skip)
   auto load_stage = [&](int s) {
 #pragma unroll
     for (int i = 0; i < kPfLoads; ++i) {
@@ -136,6 +150,26 @@ void prefill_kernel(PrefillArgs a) {
       const int64_t off = (int64_t)key * row_stride + (p & 15) * 8;
       stk[i] = *reinterpret_cast<const u32x4 *>(kg + off);
       stv[i] = *reinterpret_cast<const u32x4 *>(vg + off);
+      if constexpr (kFused) {
+        spage[i] = 0;
+        const int j = k_lo + s * kPfBN + (p >> 4) - tl.doc_start;  // position in the document
+        const int blk = j >> a.page_shift;
+        if (scatter && k_lo + s * kPfBN + (p >> 4) < k_hi && blk < a.max_blocks)
+          spage[i] = a.page_table[(int64_t)slot * a.max_blocks + blk];
+      }
+    }
+  };
+  auto scatter_stage = [&](int s) {
+#pragma unroll
+    for (int i = 0; i < kPfLoads; ++i) {
+      const int p = threadIdx.x + kPfThreads * i;
+      if (spage[i] > 0 && spage[i] < a.num_pages) {
+        const int j = k_lo + s * kPfBN + (p >> 4) - tl.doc_start;
+        const int64_t row = (int64_t)g * a.plane_rows + ((int64_t)spage[i] << a.page_shift) +
+                            (j & ((1 << a.page_shift) - 1));
+        *reinterpret_cast<u32x4 *>(a.k_pool + row * D + (p & 15) * 8) = stk[i];
+        *reinterpret_cast<u32x4 *>(a.v_pool + row * D + (p & 15) * 8) = stv[i];
+      }
     }
   };
   auto store_stage = [&](int s, int buf) {
@@ -162,6 +196,9 @@ void prefill_kernel(PrefillArgs a) {
   const int q_first = tl.q_lo;  // smallest query row of the tile
   load_stage(0);
   store_stage(0, 0);
+  if constexpr (kFused) {
+    if (scatter) scatter_stage(0);
+  }
   __syncthreads();
   for (int s = 0; s < nsteps; ++s) {
     const int buf = s & 1;
@@ -264,7 +301,12 @@ void prefill_kernel(PrefillArgs a) {
       qk(h2, sc);
       softmax_pv(h2, sc);
     }
-    if (s + 1 < nsteps) store_stage(s + 1, buf ^ 1);
+    if (s + 1 < nsteps) {
+      store_stage(s + 1, buf ^ 1);
+      if constexpr (kFused) {
+        if (scatter) scatter_stage(s + 1);
+      }
+    }
     __syncthreads();
   }
 
@@ -290,14 +332,16 @@ void prefill_kernel(PrefillArgs a) {
   }
 }
 
-hipError_t launch_prefill(const PrefillArgs &a, int32_t num_tiles_bound, hipStream_t stream) {
-  (void)num_tiles_bound;
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
   if (a.L == 0) return hipSuccess;
   const int QT = kPfRows / a.G;
   // Sum over documents of ceil(n_d / QT) is at most ceil(L / QT) + num_docs.
   const int64_t tiles = ((int64_t)a.L + QT - 1) / QT + a.num_docs;
-  const int64_t blocks = tiles * a.H_kv;
-  hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)blocks), dim3(kPfThreads), 0, stream, a);
+  const dim3 grid((unsigned)(tiles * a.H_kv));
+  if (a.k_pool)
+    hipLaunchKernelGGL(prefill_kernel<true>, grid, dim3(kPfThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(prefill_kernel<false>, grid, dim3(kPfThreads), 0, stream, a);
   return hipGetLastError();
 }
 

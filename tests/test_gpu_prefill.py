@@ -106,3 +106,76 @@ def test_prefill_then_decode_through_pages():
     check_close(d_out, d_lse, out.index_select(0, last_t).float().cpu().numpy().astype(np.float64),
                 lse.index_select(0, last_t).cpu().numpy().astype(np.float64),
                 "decode vs prefill (GPU both)")
+
+
+# ----------------------------------------------------------------------------- fused scatter
+def _run_fused(pc, doc_slots, kp0, vp0, page_table=None):
+    kd, vd = dev_bf16(kp0), dev_bf16(vp0)
+    pt = pc.page_table if page_table is None else page_table
+    out, lse = pkv.packed_prefill_attn_append(
+        dev_bf16(pc.q), dev_bf16(pc.k), dev_bf16(pc.v), dev_i32(pc.cu_seqlens),
+        float(pc.scale), kd, vd, dev_i32(pt), dev_i32(doc_slots), pc.page_size)
+    torch.cuda.synchronize()
+    return out, lse, host_bits(kd), host_bits(vd)
+
+
+def _pools(pc):
+    shape = (pc.H_kv, pc.num_pages * pc.page_size, pc.D)
+    return np.full(shape, BF16_NAN, np.uint16), np.full(shape, BF16_NAN, np.uint16)
+
+
+def test_prefill_fused_scatter_64_docs():
+    """The 64-document workload through packed_prefill_attn_append: outputs as the oracle's
+    prefill, pools byte-equal to the oracle's scatter of every token."""
+    print("prefill fused cfg5", flush=True)
+    pc, (out_ref, lse_ref) = _cfg5()
+    kp0, vp0 = _pools(pc)
+    slots = np.arange(1, pc.n_docs + 1, dtype=np.int32)
+    out, lse, kb, vb = _run_fused(pc, slots, kp0, vp0)
+    check_close(out, lse, out_ref, lse_ref, "prefill fused cfg5")
+    kr, vr = oracle.append_pages(kp0, vp0, pc.num_pages, pc.page_size, pc.page_table, pc.batch_idx,
+                                 pc.input_pos, pc.k, pc.v)
+    assert np.array_equal(kb, kr) and np.array_equal(vb, vr)
+
+
+FUSED_EDGE = [
+    # (seed, doc_lens, page_size, max_blocks)
+    (71, [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129], 16, 16),   # many pages per document
+    (72, [0, 5, 0, 70, 0], 32, 4),                                   # empty documents
+    (73, [300, 1, 17], 64, 8),
+    (74, [1000], 128, 8),                                            # one long document
+]
+
+
+@pytest.mark.parametrize("spec", FUSED_EDGE, ids=[f"seed{s[0]}" for s in FUSED_EDGE])
+def test_prefill_fused_scatter_edges(spec):
+    """Shapes as above plus the skip rules: a document in slot 0, a document whose later
+    blocks are unmapped (page 0), a slot beyond the table, and a document longer than
+    the table (blocks past max_blocks)."""
+    seed, lens, ps, mb = spec
+    print(f"prefill fused edge seed={seed}", flush=True)
+    pc = make_prefill_case(name="fedge", seed=seed, doc_lens=lens, H_q=32, H_kv=8, D=128,
+                           page_size=ps, num_pages=sum(-(-n // ps) for n in lens) + 4,
+                           max_blocks=max(-(-max(lens) // ps), 1))
+    out_ref, lse_ref = oracle.prefill_case(pc)
+    slots = np.arange(1, pc.n_docs + 1, dtype=np.int32)
+    pt = pc.page_table.copy()
+    bidx = pc.batch_idx.copy()
+    if pc.n_docs >= 2:
+        slots[0] = 0                                   # document 0 in the padding slot
+        bidx[pc.cu_seqlens[0]:pc.cu_seqlens[1]] = 0
+    if pc.n_docs >= 3:
+        slots[-1] = pc.num_slots + 3                   # slot beyond the table
+        bidx[pc.cu_seqlens[-2]:pc.cu_seqlens[-1]] = pc.num_slots + 3
+    longest = int(np.argmax(pc.doc_lens()))
+    nb = -(-int(pc.doc_lens()[longest]) // ps)
+    if nb >= 2 and slots[longest] != 0 and slots[longest] < pc.num_slots:
+        pt[slots[longest], nb - 1] = 0                 # last block of the longest document unmapped
+    if nb >= 3 and slots[longest] != 0 and slots[longest] < pc.num_slots:
+        pt = pt[:, :nb - 1].copy()                     # ...and the table one block too narrow
+    kp0, vp0 = _pools(pc)
+    out, lse, kb, vb = _run_fused(pc, slots, kp0, vp0, page_table=pt)
+    check_close(out, lse, out_ref, lse_ref, f"prefill fused seed{seed}")
+    kr, vr = oracle.append_pages(kp0, vp0, pc.num_pages, pc.page_size, pt, bidx, pc.input_pos,
+                                 pc.k, pc.v)
+    assert np.array_equal(kb, kr) and np.array_equal(vb, vr)
