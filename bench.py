@@ -66,6 +66,8 @@ def parse():
     ap.add_argument("--flush", action="store_true",
                     help="time each call alone after a 1 GiB read of another buffer")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-chunked", action="store_true",
+                    help="skip the chunked-prefill (paged prefix) measurement")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="budget for the CPU oracle baseline (0 = skip)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -221,6 +223,31 @@ def main():
                        step=prefill_step_separate if args.separate else prefill_step_fused,
                        alt=prefill_step_fused if args.separate else prefill_step_separate)
 
+    # ---------------- chunked prefill over a paged prefix (64 sequences), one pool set per layer
+    chunked = None
+    if not args.no_chunked:
+        from workloads import make_chunked_prefill_case
+        crng = np.random.default_rng(9305)
+        cc = make_chunked_prefill_case(name="chunked", seed=9305,
+                                       prefix_lens=crng.integers(256, 1025, 64),
+                                       chunk_lens=crng.integers(64, 257, 64), H_q=32, H_kv=8,
+                                       D=128, page_size=128, fill="empty", rng=crng)
+        NC = max(1, args.prefill_layers)
+        c_kp = [dev_bf16(cc.k_pool) for _ in range(NC)]
+        c_vp = [dev_bf16(cc.v_pool) for _ in range(NC)]
+        c_q, c_k, c_v = dev_bf16(cc.q), dev_bf16(cc.k), dev_bf16(cc.v)
+        c_cu, c_pl = dev_i32(cc.cu_seqlens), dev_i32(cc.prefix_lens)
+        c_sl, c_pt = dev_i32(cc.doc_slots), dev_i32(cc.page_table)
+        c_out = torch.empty((cc.L, cc.H_q, cc.D), dtype=torch.bfloat16, device=dev)
+        c_lse = torch.empty((cc.L, cc.H_q), dtype=torch.float32, device=dev)
+
+        def chunked_step(i):
+            j = i % NC
+            pkv.paged_prefill_attn(c_q, c_k, c_v, c_cu, c_pl, c_sl, float(cc.scale), c_kp[j],
+                                   c_vp[j], c_pt, cc.page_size, out=c_out, lse=c_lse)
+
+        chunked = dict(case=cc, step=chunked_step, layers=NC)
+
     flush_buf = torch.ones(1024 * 1024 * 1024 // 4, dtype=torch.float32, device=dev) \
         if args.flush else None
     flush_sink = torch.empty((), dtype=torch.float32, device=dev)
@@ -272,6 +299,8 @@ def main():
         decode_step(i)
         if prefill:
             prefill["step"](i)
+        if chunked:
+            chunked["step"](i)
     torch.cuda.synchronize()
 
     # ---------------- timed steps
@@ -286,6 +315,7 @@ def main():
     alt_total = timed(decode_step_fused if args.separate else decode_step_separate, K)
     pa_total = timed(prefill["attn"], K) if prefill else 0.0
     palt_total = timed(prefill["alt"], K) if prefill else 0.0
+    ch_total = timed(chunked["step"], K) if chunked else 0.0
 
     dec_ms, dk_ms = dec_total / K, dk_total / K
     value = kv_bytes / (dec_ms * 1e-3) / 1e9
@@ -362,6 +392,21 @@ def main():
                 "traffic": measured_traffic("prefill", "prefill.hip"),
             },
             "cache": f"cold: {prefill['layers']} input sets read round-robin",
+        }
+    if chunked:
+        cc = chunked["case"]
+        ch_ms = ch_total / K
+        kv_prefix = int(cc.prefix_lens.astype(np.int64).sum()) * cc.H_kv * cc.D * 2 * 2
+        out["chunked_prefill"] = {
+            "workload": "chunked prefill over a paged prefix: 64 sequences with U[256,1024] "
+                        "cached tokens, chunks U[64,256] (L=%d), H_q=32 H_kv=8 D=128, "
+                        "page_size=128 shuffled; chunk K/V written into the pages" % cc.L,
+            "call": "paged_prefill_attn",
+            "us": round(ch_ms * 1e3, 3),
+            "flops_per_call": int(cc.flops()),
+            "tflops": round(cc.flops() / (ch_ms * 1e-3) / 1e12, 2),
+            "prefix_kv_bytes": kv_prefix,
+            "cache": f"cold: {chunked['layers']} pool sets read round-robin",
         }
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(c, kv_bytes, args.cpu_seconds)

@@ -252,6 +252,47 @@ int packed_prefill_attn_append(const void *q, const void *k, const void *v,
                                int32_t num_slots, int32_t max_blocks, const int32_t *doc_slots,
                                void *stream);
 
+/*
+ * paged_prefill_attn - chunked prefill over a paged prefix.
+ *
+ * The results write-up (flex_vs_vllm.md, "What's left on the table") names
+ * chunked prefill, where new prompt chunks are processed against sequences
+ * whose earlier tokens are already cached, as the main remaining penalty for
+ * large batches.  Document d is a chunk of n_d = cu_seqlens[d+1] -
+ * cu_seqlens[d] new tokens (those rows of q, k, v) continuing the sequence in
+ * batch slot doc_slots[d], whose first prefix_lens[d] tokens are already in
+ * the pools.  Chunk token j has position prefix_lens[d] + j: it is written
+ * into its page as paged_kv_append would, and it attends to positions
+ * 0 .. prefix_lens[d] + j of its sequence (the cached prefix through the
+ * page table, the chunk causally; GQA and scale as in decode).  Equivalent to
+ *     paged_kv_append(chunk tokens at their positions) ;
+ *     for every chunk row: paged_decode_attn with kv_len = position + 1
+ * Rows of a document whose slot is 0 or not below num_slots return
+ * (+0, -inf).  With every prefix 0 the result is packed_prefill_attn_append.
+ *
+ *   q                bf16 [total_len][num_q_heads][head_dim]
+ *   k, v             bf16 [total_len][num_kv_heads][head_dim], the chunks' K/V
+ *   cu_seqlens       int32 [num_docs+1] as in packed_prefill_attn
+ *   prefix_lens      int32 [num_docs], device; clamped to [0, max_blocks*page_size]
+ *   doc_slots        int32 [num_docs], device
+ *   k_pool, v_pool   bf16 [num_kv_heads][num_pages*page_size][head_dim];
+ *                    read (prefix) and written (chunk)
+ *   page_table       int32 [num_slots][max_blocks]
+ *   out, lse         as in packed_prefill_attn
+ *
+ * The pages of a sequence's positions 0 .. prefix + n_d - 1 must be mapped
+ * (pages 1..num_pages-1) and lie within max_blocks*page_size; otherwise
+ * results are unspecified (no access leaves the buffers).  Requirements:
+ * those of packed_prefill_attn and paged_kv_append.
+ */
+int paged_prefill_attn(const void *q, const void *k, const void *v, const int32_t *cu_seqlens,
+                       const int32_t *prefix_lens, const int32_t *doc_slots, int32_t num_docs,
+                       int32_t total_len, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, float scale, void *k_pool, void *v_pool,
+                       int32_t num_pages, int32_t page_size, const int32_t *page_table,
+                       int32_t num_slots, int32_t max_blocks, void *out, float *lse,
+                       void *stream);
+
 /* Text for the most recent non-zero status returned on this thread. */
 const char *pkv_last_error(void);
 

@@ -14,6 +14,8 @@ libpkv.so (include/pkv.h):
   packed_prefill_attn_append
                        the prefill plus the scatter of the prompts' K/V
                        into their pages, in one launch
+  paged_prefill_attn   chunked prefill: chunks attend to their sequence's
+                       cached prefix (pages) and to themselves causally
 
 This package is the thin Python binding: it marshals torch tensors into the
 C calls and nothing else.
@@ -34,4 +36,5 @@ from ._binding import (  # noqa: F401
     paged_decode_num_splits,
     paged_decode_workspace_size,
     paged_kv_append,
+    paged_prefill_attn,
 )

@@ -78,6 +78,10 @@ def load_library(path: str = LIB_PATH):
                                              ctypes.c_float, _P, _P, _P, _P, _I32, _I32, _P,
                                              _I32, _I32, _P, _P]
     L.packed_prefill_attn_append.restype = ctypes.c_int
+    L.paged_prefill_attn.argtypes = [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                     ctypes.c_float, _P, _P, _I32, _I32, _P, _I32, _I32, _P, _P,
+                                     _P]
+    L.paged_prefill_attn.restype = ctypes.c_int
     L.pkv_last_error.argtypes = []
     L.pkv_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -291,4 +295,41 @@ def packed_prefill_attn_append(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
         _dev(page_table, "page_table", torch.int32, 2), num_slots, max_blocks,
         _dev(doc_slots, "doc_slots", torch.int32, 1), _stream(stream))
     _check(rc, "packed_prefill_attn_append")
+    return out, lse
+
+
+def paged_prefill_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+                       prefix_lens: torch.Tensor, doc_slots: torch.Tensor, scale: float,
+                       k_pool: torch.Tensor, v_pool: torch.Tensor, page_table: torch.Tensor,
+                       page_size: int, out: Optional[torch.Tensor] = None,
+                       lse: Optional[torch.Tensor] = None,
+                       stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Chunked prefill: chunk rows attend to their sequence's cached prefix (pages) and to
+    the chunk causally; the chunk's K/V are written into the pages.  Returns (out, lse)."""
+    L = load_library()
+    Lt, H_q, D = q.shape
+    _, H_kv, _ = k.shape
+    if tuple(k.shape) != (Lt, H_kv, D) or tuple(v.shape) != (Lt, H_kv, D):
+        raise ValueError("k/v must be [L, H_kv, D] matching q")
+    Hp, rows, Dp = k_pool.shape
+    if Hp != H_kv or Dp != D or v_pool.shape != k_pool.shape or rows % page_size:
+        raise ValueError("pool shape does not match k / page_size")
+    n_docs = cu_seqlens.shape[0] - 1
+    if doc_slots.shape[0] != n_docs or prefix_lens.shape[0] != n_docs:
+        raise ValueError("doc_slots and prefix_lens must have one entry per document")
+    num_slots, max_blocks = page_table.shape
+    if out is None:
+        out = torch.empty((Lt, H_q, D), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((Lt, H_q), dtype=torch.float32, device=q.device)
+    rc = L.paged_prefill_attn(
+        _dev(q, "q", torch.bfloat16, 3), _dev(k, "k", torch.bfloat16, 3),
+        _dev(v, "v", torch.bfloat16, 3), _dev(cu_seqlens, "cu_seqlens", torch.int32, 1),
+        _dev(prefix_lens, "prefix_lens", torch.int32, 1),
+        _dev(doc_slots, "doc_slots", torch.int32, 1), n_docs, Lt, H_q, H_kv, D, float(scale),
+        _dev(k_pool, "k_pool", torch.bfloat16, 3), _dev(v_pool, "v_pool", torch.bfloat16, 3),
+        rows // page_size, page_size, _dev(page_table, "page_table", torch.int32, 2), num_slots,
+        max_blocks, _dev(out, "out", torch.bfloat16, 3), _dev(lse, "lse", torch.float32, 2),
+        _stream(stream))
+    _check(rc, "paged_prefill_attn")
     return out, lse

@@ -318,7 +318,7 @@ static int prefill_common(const char *who, const void *q, const void *k, const v
                           void *out, float *lse, bool fused, void *k_pool, void *v_pool,
                           int32_t num_pages, int32_t page_size, const int32_t *page_table,
                           int32_t num_slots, int32_t max_blocks, const int32_t *doc_slots,
-                          void *stream) {
+                          const int32_t *prefix_lens, void *stream) {
   if (total_len < 0 || num_docs < 0)
     return fail(PKV_E_SHAPE, "total_len and num_docs must be >= 0 (got %d, %d)", total_len, num_docs);
   if (head_dim != 128) return fail(PKV_E_SHAPE, "%s supports head_dim 128 (got %d)", who, head_dim);
@@ -336,13 +336,15 @@ static int prefill_common(const char *who, const void *q, const void *k, const v
   if (total_len == 0) return PKV_OK;
   if (num_docs == 0) return fail(PKV_E_SHAPE, "total_len > 0 needs at least one document");
   if (!q || !k || !v || !cu_seqlens || !out || !lse ||
-      (fused && (!k_pool || !v_pool || !page_table || !doc_slots)))
+      (fused && (!k_pool || !v_pool || !page_table || !doc_slots)) ||
+      (prefix_lens && !fused))
     return fail(PKV_E_NULL, "%s: a required pointer is NULL", who);
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
       (fused && (!aligned16(k_pool) || !aligned16(v_pool))))
     return fail(PKV_E_ALIGN, "%s: bf16 tensors must be 16-byte aligned", who);
   if (!aligned4(cu_seqlens) || !aligned4(lse) ||
-      (fused && (!aligned4(page_table) || !aligned4(doc_slots))))
+      (fused && (!aligned4(page_table) || !aligned4(doc_slots))) ||
+      (prefix_lens && !aligned4(prefix_lens)))
     return fail(PKV_E_ALIGN, "%s: int32/fp32 tensors must be 4-byte aligned", who);
   pkv::PrefillArgs a;
   a.q = (const uint16_t *)q;
@@ -361,6 +363,7 @@ static int prefill_common(const char *who, const void *q, const void *k, const v
   a.v_pool = fused ? (uint16_t *)v_pool : nullptr;
   a.page_table = fused ? page_table : nullptr;
   a.doc_slots = fused ? doc_slots : nullptr;
+  a.prefix_lens = fused ? prefix_lens : nullptr;
   a.plane_rows = fused ? (int64_t)num_pages * page_size : 0;
   a.num_pages = num_pages;
   a.page_shift = fused ? log2_exact(page_size) : 0;
@@ -375,7 +378,7 @@ int packed_prefill_attn(const void *q, const void *k, const void *v, const int32
                         float *lse, void *stream) {
   return prefill_common("packed_prefill_attn", q, k, v, cu_seqlens, num_docs, total_len,
                         num_q_heads, num_kv_heads, head_dim, scale, out, lse, false, nullptr,
-                        nullptr, 0, 0, nullptr, 0, 0, nullptr, stream);
+                        nullptr, 0, 0, nullptr, 0, 0, nullptr, nullptr, stream);
 }
 
 int packed_prefill_attn_append(const void *q, const void *k, const void *v,
@@ -387,7 +390,23 @@ int packed_prefill_attn_append(const void *q, const void *k, const void *v,
                                void *stream) {
   return prefill_common("packed_prefill_attn_append", q, k, v, cu_seqlens, num_docs, total_len,
                         num_q_heads, num_kv_heads, head_dim, scale, out, lse, true, k_pool, v_pool,
-                        num_pages, page_size, page_table, num_slots, max_blocks, doc_slots, stream);
+                        num_pages, page_size, page_table, num_slots, max_blocks, doc_slots,
+                        nullptr, stream);
+}
+
+int paged_prefill_attn(const void *q, const void *k, const void *v, const int32_t *cu_seqlens,
+                       const int32_t *prefix_lens, const int32_t *doc_slots, int32_t num_docs,
+                       int32_t total_len, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, float scale, void *k_pool, void *v_pool,
+                       int32_t num_pages, int32_t page_size, const int32_t *page_table,
+                       int32_t num_slots, int32_t max_blocks, void *out, float *lse,
+                       void *stream) {
+  if (total_len > 0 && !prefix_lens)
+    return fail(PKV_E_NULL, "paged_prefill_attn: a required pointer is NULL");
+  return prefill_common("paged_prefill_attn", q, k, v, cu_seqlens, num_docs, total_len,
+                        num_q_heads, num_kv_heads, head_dim, scale, out, lse, true, k_pool, v_pool,
+                        num_pages, page_size, page_table, num_slots, max_blocks, doc_slots,
+                        prefix_lens, stream);
 }
 
 }  // extern "C"

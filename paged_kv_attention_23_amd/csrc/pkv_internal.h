@@ -54,6 +54,7 @@ struct PrefillArgs {
   uint16_t *k_pool, *v_pool;       // [H_kv][plane_rows][D]
   const int32_t *page_table;       // [num_slots][max_blocks]
   const int32_t *doc_slots;        // [num_docs]
+  const int32_t *prefix_lens;      // [num_docs] cached tokens before each chunk; NULL: none
   int64_t plane_rows;
   int32_t num_pages, page_shift, num_slots, max_blocks;
 };

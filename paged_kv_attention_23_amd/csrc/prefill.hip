@@ -87,9 +87,10 @@ __device__ bool find_tile(const int32_t *cu, int num_docs, int QT, int qt_shift,
   return false;
 }
 
-template <bool kFused>
+template <bool kFused, bool kPrefix>
 __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_kernel(PrefillArgs a) {
+  static_assert(kFused || !kPrefix, "a paged prefix comes with the chunk's scatter");
   __shared__ __attribute__((aligned(16))) char smem[kPfSmem];
   constexpr int D = kPfD;
   const int lane = threadIdx.x & (kWave - 1);
@@ -103,20 +104,43 @@ void prefill_kernel(PrefillArgs a) {
 
   PfTile tl;
   if (!find_tile(a.cu_seqlens, a.num_docs, QT, qt_shift, tile, lane, tl)) return;  // uniform
-  const int k_lo = tl.doc_start, k_hi = tl.q_hi;
-  // Fused scatter: the document's last query tile reads every key of the
-  // document (its key range ends at the document end), so it alone writes
-  // the document's K/V rows of this head into their pages, from the stage
-  // registers.  Skip rules as in paged_kv_append.
-  int slot = 0;
+  // Keys are numbered by their position in the sequence: [0, prefix) are
+  // cached in the pages (paged prefix, chunked prefill), [prefix, k_end) are
+  // this document's packed rows, position prefix + j at packed row
+  // doc_start + j.  Without a paged prefix, prefix = 0.
+  // Fused scatter: the document's last query tile reads every packed key of
+  // the document (its key range ends at the document end), so it alone
+  // writes them into their pages, from the stage registers.  Skip rules as
+  // in paged_kv_append.
+  int slot = 0, prefix = 0;
   bool scatter = false;
   if constexpr (kFused) {
     slot = a.doc_slots[tl.doc];
-    scatter = tl.q_hi == tl.doc_end && slot > 0 && slot < a.num_slots;
+    const bool slot_ok = slot > 0 && slot < a.num_slots;
+    if constexpr (kPrefix) {
+      if (!slot_ok) {  // padding document: every row sees no key (+0, -inf)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const int R = 32 * wave + 16 * qb + hl;
+          const int hh = qt_shift >= 0 ? R >> qt_shift : R / QT;
+          const int qq = tl.q_lo + (qt_shift >= 0 ? R & (QT - 1) : R % QT);
+          if (hh >= G || qq >= tl.q_hi) continue;
+          const int64_t rh = (int64_t)qq * a.H_q + g * G + hh;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<u32x4 *>(a.out + rh * kPfD + 32 * lg + 8 * i) = u32x4{0u, 0u, 0u, 0u};
+          if (lg == 0) a.lse[rh] = -INFINITY;
+        }
+        return;
+      }
+      prefix = min(max(a.prefix_lens[tl.doc], 0), a.max_blocks << a.page_shift);
+    }
+    scatter = tl.q_hi == tl.doc_end && slot_ok;
   }
+  const int k_end = prefix + (tl.q_hi - tl.doc_start);
 
   // Rows of this wave: column block qb, column hl -> tile row R.
-  int col_head[2], col_q[2];
+  int col_head[2], col_q[2], col_pos[2];
   bool col_ok[2];
   bf16x8 qop[2][D / 32];
 #pragma unroll
@@ -126,7 +150,8 @@ void prefill_kernel(PrefillArgs a) {
     const int qq = tl.q_lo + (qt_shift >= 0 ? R & (QT - 1) : R % QT);
     col_ok[qb] = (hh < G) && (qq < tl.q_hi);
     col_head[qb] = g * G + min(hh, G - 1);
-    col_q[qb] = col_ok[qb] ? qq : k_lo - 1;  // unused columns mask every key
+    col_q[qb] = col_ok[qb] ? qq : tl.q_lo;
+    col_pos[qb] = col_ok[qb] ? prefix + (qq - tl.doc_start) : -1;  // -1: masks every key
     const uint16_t *qr = a.q + ((int64_t)col_q[qb] * a.H_q + col_head[qb]) * D + 8 * lg;
 #pragma unroll
     for (int ch = 0; ch < D / 32; ++ch) {
@@ -146,15 +171,24 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < kPfLoads; ++i) {
       const int p = threadIdx.x + kPfThreads * i;
-      const int key = min(k_lo + s * kPfBN + (p >> 4), k_hi - 1);
-      const int64_t off = (int64_t)key * row_stride + (p & 15) * 8;
-      stk[i] = *reinterpret_cast<const u32x4 *>(kg + off);
-      stv[i] = *reinterpret_cast<const u32x4 *>(vg + off);
+      const int pos = s * kPfBN + (p >> 4);   // key position
+      const int key = min(pos, k_end - 1);
+      if (kPrefix && key < prefix) {          // cached prefix: through the page table
+        int page = a.page_table[(int64_t)slot * a.max_blocks + (key >> a.page_shift)];
+        page = min(max(page, 0), a.num_pages - 1);
+        const int64_t row = (int64_t)g * a.plane_rows + ((int64_t)page << a.page_shift) +
+                            (key & ((1 << a.page_shift) - 1));
+        stk[i] = *reinterpret_cast<const u32x4 *>(a.k_pool + row * D + (p & 15) * 8);
+        stv[i] = *reinterpret_cast<const u32x4 *>(a.v_pool + row * D + (p & 15) * 8);
+      } else {                                // this document's packed rows
+        const int64_t off = (int64_t)(tl.doc_start + key - prefix) * row_stride + (p & 15) * 8;
+        stk[i] = *reinterpret_cast<const u32x4 *>(kg + off);
+        stv[i] = *reinterpret_cast<const u32x4 *>(vg + off);
+      }
       if constexpr (kFused) {
         spage[i] = 0;
-        const int j = k_lo + s * kPfBN + (p >> 4) - tl.doc_start;  // position in the document
-        const int blk = j >> a.page_shift;
-        if (scatter && k_lo + s * kPfBN + (p >> 4) < k_hi && blk < a.max_blocks)
+        const int blk = pos >> a.page_shift;
+        if (scatter && pos >= prefix && pos < k_end && blk < a.max_blocks)
           spage[i] = a.page_table[(int64_t)slot * a.max_blocks + blk];
       }
     }
@@ -164,9 +198,9 @@ void prefill_kernel(PrefillArgs a) {
     for (int i = 0; i < kPfLoads; ++i) {
       const int p = threadIdx.x + kPfThreads * i;
       if (spage[i] > 0 && spage[i] < a.num_pages) {
-        const int j = k_lo + s * kPfBN + (p >> 4) - tl.doc_start;
+        const int pos = s * kPfBN + (p >> 4);
         const int64_t row = (int64_t)g * a.plane_rows + ((int64_t)spage[i] << a.page_shift) +
-                            (j & ((1 << a.page_shift) - 1));
+                            (pos & ((1 << a.page_shift) - 1));
         *reinterpret_cast<u32x4 *>(a.k_pool + row * D + (p & 15) * 8) = stk[i];
         *reinterpret_cast<u32x4 *>(a.v_pool + row * D + (p & 15) * 8) = stv[i];
       }
@@ -178,7 +212,7 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < kPfLoads; ++i) {
       const int p = threadIdx.x + kPfThreads * i;
-      const bool live = k_lo + s * kPfBN + (p >> 4) < k_hi;
+      const bool live = s * kPfBN + (p >> 4) < k_end;
       const int off = (p >> 4) * kPfRowStride + (p & 15) * 16;
       *reinterpret_cast<u32x4 *>(kb + off) = live ? stk[i] : u32x4{0u, 0u, 0u, 0u};
       *reinterpret_cast<u32x4 *>(vb + off) = live ? stv[i] : u32x4{0u, 0u, 0u, 0u};
@@ -192,8 +226,8 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) o[qb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nsteps = (k_hi - k_lo + kPfBN - 1) / kPfBN;
-  const int q_first = tl.q_lo;  // smallest query row of the tile
+  const int nsteps = (k_end + kPfBN - 1) / kPfBN;
+  const int q_first = prefix + (tl.q_lo - tl.doc_start);  // position of the tile's first row
   load_stage(0);
   store_stage(0, 0);
   if constexpr (kFused) {
@@ -223,7 +257,7 @@ void prefill_kernel(PrefillArgs a) {
       }
     };
     auto softmax_pv = [&](int h2, const f32x4 (&sc)[2][2]) {
-      const int key0 = k_lo + s * kPfBN + 32 * h2;
+      const int key0 = s * kPfBN + 32 * h2;  // position of the half's first key
       const bool diag = key0 + 31 >= q_first;  // some key may lie past some query row
       // V^T operands: lane reads V[key kappa(lg, e)][8*hl .. 8*hl+7]; step t
       // uses head_dim d = 8*m + t for its row m.
@@ -246,7 +280,7 @@ void prefill_kernel(PrefillArgs a) {
           x[4 + i] = sc[1][qb][i];
         }
         if (diag) {
-          const int lim = col_q[qb] - key0 - 4 * lg;  // key offset i is live iff i <= lim
+          const int lim = col_pos[qb] - key0 - 4 * lg;  // key offset i is live iff i <= lim
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             const int off = i < 4 ? i : 16 + (i - 4);
@@ -296,7 +330,7 @@ void prefill_kernel(PrefillArgs a) {
     };
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {  // two 32-key halves of the stage
-      if (k_lo + s * kPfBN + 32 * h2 >= k_hi) break;  // uniform
+      if (s * kPfBN + 32 * h2 >= k_end) break;  // uniform
       f32x4 sc[2][2];
       qk(h2, sc);
       softmax_pv(h2, sc);
@@ -338,10 +372,12 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
   // Sum over documents of ceil(n_d / QT) is at most ceil(L / QT) + num_docs.
   const int64_t tiles = ((int64_t)a.L + QT - 1) / QT + a.num_docs;
   const dim3 grid((unsigned)(tiles * a.H_kv));
-  if (a.k_pool)
-    hipLaunchKernelGGL(prefill_kernel<true>, grid, dim3(kPfThreads), 0, stream, a);
+  if (a.prefix_lens)
+    hipLaunchKernelGGL((prefill_kernel<true, true>), grid, dim3(kPfThreads), 0, stream, a);
+  else if (a.k_pool)
+    hipLaunchKernelGGL((prefill_kernel<true, false>), grid, dim3(kPfThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(prefill_kernel<false>, grid, dim3(kPfThreads), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<false, false>), grid, dim3(kPfThreads), 0, stream, a);
   return hipGetLastError();
 }
 

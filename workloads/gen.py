@@ -265,6 +265,119 @@ def make_prefill_case(*, name: str, seed: int, doc_lens: Sequence[int], H_q: int
                        batch_idx=bidx, input_pos=ipos.astype(np.int32), meta=dict(layout=layout))
 
 
+@dataclass
+class ChunkedPrefillCase:
+    """Prompt chunks continuing sequences whose first tokens are already cached in pages."""
+
+    name: str
+    seed: int
+    H_q: int
+    H_kv: int
+    D: int
+    scale: np.float32
+    q: np.ndarray            # uint16 [L, H_q, D], the chunks packed
+    k: np.ndarray            # uint16 [L, H_kv, D]
+    v: np.ndarray            # uint16 [L, H_kv, D]
+    cu_seqlens: np.ndarray   # int32 [n+1], chunk bounds
+    prefix_lens: np.ndarray  # int32 [n], cached tokens before each chunk
+    doc_slots: np.ndarray    # int32 [n], batch slot of each sequence (0 = padding)
+    page_size: int
+    num_pages: int
+    num_slots: int
+    max_blocks: int
+    page_table: np.ndarray   # int32 [num_slots, max_blocks]
+    k_pool: np.ndarray       # uint16 [H_kv, num_pages*page_size, D], the cached prefixes
+    v_pool: np.ndarray
+    batch_idx: np.ndarray    # int32 [L], slot of each chunk token
+    input_pos: np.ndarray    # int32 [L], position of each chunk token in its sequence
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def L(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def n_docs(self) -> int:
+        return int(self.cu_seqlens.shape[0] - 1)
+
+    def flops(self) -> int:
+        """4*D*H_q per (query, key) pair a live chunk row attends to (prefix + causal chunk)."""
+        live = self.doc_slots[self.batch_idx_doc()] != 0
+        return 4 * self.D * self.H_q * int((self.input_pos[live].astype(np.int64) + 1).sum())
+
+    def batch_idx_doc(self) -> np.ndarray:
+        """Document of each chunk token."""
+        return np.repeat(np.arange(self.n_docs), np.diff(self.cu_seqlens.astype(np.int64)))
+
+
+def make_chunked_prefill_case(*, name: str, seed: int, prefix_lens: Sequence[int],
+                              chunk_lens: Sequence[int], H_q: int, H_kv: int, D: int,
+                              page_size: int, slots: Optional[Sequence[int]] = None,
+                              num_pages: Optional[int] = None, max_blocks: Optional[int] = None,
+                              layout: str = "shuffled", fill: str = "nan",
+                              rng: Optional[np.random.Generator] = None,
+                              scale: Optional[float] = None) -> ChunkedPrefillCase:
+    """Build one chunked-prefill step.
+
+    Sequence d lives in slot slots[d] (default d+1; 0 = padding) and owns
+    ceil((prefix_d + chunk_d) / page_size) pages, assigned in the layout's
+    order; its prefix K/V (positions 0..prefix_d-1) are drawn and written into
+    the pools, whose other bytes hold `fill` ('nan', 'zero' or 'empty').
+    Draw order: page permutation, prefix K, prefix V, chunk q, k, v.
+    """
+    rng = rng if rng is not None else np.random.Generator(np.random.PCG64(seed))
+    prefix = np.asarray(prefix_lens, dtype=np.int32)
+    chunk = np.asarray(chunk_lens, dtype=np.int32)
+    n = int(prefix.shape[0])
+    slots = np.asarray(slots if slots is not None else np.arange(1, n + 1), dtype=np.int32)
+    live = [d for d in range(n) if slots[d] != 0]
+    if len(set(int(slots[d]) for d in live)) != len(live):
+        raise ValueError("live sequences must use distinct slots")
+    blocks = [-(-int(prefix[d] + chunk[d]) // page_size) for d in live]
+    mb = max_blocks if max_blocks is not None else max(blocks + [1])
+    if any(b > mb for b in blocks):
+        raise ValueError("sequence longer than max_blocks*page_size")
+    P = num_pages if num_pages is not None else sum(blocks) + 2
+    pages = _assign_pages(rng, [int(slots[d]) for d in live], blocks, P, layout)
+    num_slots = int(slots.max()) + 1 if n else 1
+    pt = np.zeros((num_slots, mb), dtype=np.int32)
+    for d, pg in zip(live, pages):
+        pt[slots[d], :len(pg)] = pg
+    rows_total = P * page_size
+    if fill == "nan":
+        k_pool = np.full((H_kv, rows_total, D), BF16_NAN, dtype=np.uint16)
+    elif fill in ("zero", "empty"):
+        k_pool = np.zeros((H_kv, rows_total, D), dtype=np.uint16)
+    else:
+        raise ValueError(fill)
+    v_pool = k_pool.copy()
+    phys = []
+    for d, pg in zip(live, pages):
+        j = np.arange(int(prefix[d]), dtype=np.int64)
+        phys.append(pg[j // page_size].astype(np.int64) * page_size + j % page_size)
+    phys_all = np.concatenate(phys) if phys else np.zeros(0, dtype=np.int64)
+    pk = _normal_bf16(rng, (phys_all.shape[0], H_kv, D))
+    pv = _normal_bf16(rng, (phys_all.shape[0], H_kv, D))
+    for h in range(H_kv):
+        k_pool[h, phys_all, :] = pk[:, h, :]
+        v_pool[h, phys_all, :] = pv[:, h, :]
+    cu = np.zeros(n + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(chunk)
+    L = int(cu[-1])
+    q = _normal_bf16(rng, (L, H_q, D))
+    k = _normal_bf16(rng, (L, H_kv, D))
+    v = _normal_bf16(rng, (L, H_kv, D))
+    bidx = np.repeat(slots, chunk).astype(np.int32)
+    ipos = np.concatenate([int(prefix[d]) + np.arange(int(chunk[d]), dtype=np.int32)
+                           for d in range(n)]).astype(np.int32) if n else np.zeros(0, np.int32)
+    sc = np.float32(scale if scale is not None else 1.0 / np.sqrt(D))
+    return ChunkedPrefillCase(name=name, seed=seed, H_q=H_q, H_kv=H_kv, D=D, scale=sc, q=q, k=k,
+                              v=v, cu_seqlens=cu, prefix_lens=prefix, doc_slots=slots,
+                              page_size=page_size, num_pages=P, num_slots=num_slots,
+                              max_blocks=mb, page_table=pt, k_pool=k_pool, v_pool=v_pool,
+                              batch_idx=bidx, input_pos=ipos, meta=dict(layout=layout, fill=fill))
+
+
 # ---------------------------------------------------------------------------
 # The five named workloads.  Seeds are 2300 + config number.  "Uniform in
 # [a, b]" means integers, both ends included.
