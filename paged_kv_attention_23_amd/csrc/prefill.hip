@@ -32,11 +32,22 @@
 
 namespace pkv {
 
+#ifndef PKV_PF_QB
+#define PKV_PF_QB 2
+#endif
+#ifndef PKV_PF_BN
+#define PKV_PF_BN 64
+#endif
+#ifndef PKV_PF_WPE
+#define PKV_PF_WPE 2
+#endif
 constexpr int kPfD = 128;
 constexpr int kPfWaves = 4;
 constexpr int kPfThreads = kPfWaves * kWave;
-constexpr int kPfRows = 128;                         // (head, query) rows per workgroup
-constexpr int kPfBN = 64;                            // keys per LDS stage
+constexpr int kQB = PKV_PF_QB;                       // 16-column blocks per wave
+constexpr int kPfRows = 16 * kQB * kPfWaves;         // (head, query) rows per workgroup
+constexpr int kPfBN = PKV_PF_BN;                     // keys per LDS stage (multiple of 32)
+constexpr int kHalves = kPfBN / 32;                  // 32-key steps per stage
 constexpr int kPfRowStride = 2 * kPfD + 16;          // bytes per key row in LDS
 constexpr int kPfTileBytes = kPfBN * kPfRowStride;   // one K or V stage
 constexpr int kPfSmem = 2 * 2 * kPfTileBytes;        // 2 stages x (K, V)
@@ -88,7 +99,7 @@ __device__ bool find_tile(const int32_t *cu, int num_docs, int QT, int qt_shift,
 }
 
 template <bool kFused, bool kPrefix>
-__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(PKV_PF_WPE)))
 void prefill_kernel(PrefillArgs a) {
   static_assert(kFused || !kPrefix, "a paged prefix comes with the chunk's scatter");
   __shared__ __attribute__((aligned(16))) char smem[kPfSmem];
@@ -120,8 +131,8 @@ void prefill_kernel(PrefillArgs a) {
     if constexpr (kPrefix) {
       if (!slot_ok) {  // padding document: every row sees no key (+0, -inf)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const int R = 32 * wave + 16 * qb + hl;
+        for (int qb = 0; qb < kQB; ++qb) {
+          const int R = 16 * kQB * wave + 16 * qb + hl;
           const int hh = qt_shift >= 0 ? R >> qt_shift : R / QT;
           const int qq = tl.q_lo + (qt_shift >= 0 ? R & (QT - 1) : R % QT);
           if (hh >= G || qq >= tl.q_hi) continue;
@@ -140,12 +151,12 @@ void prefill_kernel(PrefillArgs a) {
   const int k_end = prefix + (tl.q_hi - tl.doc_start);
 
   // Rows of this wave: column block qb, column hl -> tile row R.
-  int col_head[2], col_q[2], col_pos[2];
-  bool col_ok[2];
-  bf16x8 qop[2][D / 32];
+  int col_head[kQB], col_q[kQB], col_pos[kQB];
+  bool col_ok[kQB];
+  bf16x8 qop[kQB][D / 32];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int R = 32 * wave + 16 * qb + hl;
+  for (int qb = 0; qb < kQB; ++qb) {
+    const int R = 16 * kQB * wave + 16 * qb + hl;
     const int hh = qt_shift >= 0 ? R >> qt_shift : R / QT;
     const int qq = tl.q_lo + (qt_shift >= 0 ? R & (QT - 1) : R % QT);
     col_ok[qb] = (hh < G) && (qq < tl.q_hi);
@@ -219,10 +230,15 @@ void prefill_kernel(PrefillArgs a) {
     }
   };
 
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-  f32x4 o[2][D / 16];
+  float m_run[kQB], l_run[kQB];
+  f32x4 o[kQB][D / 16];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < kQB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+  }
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) o[qb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -240,7 +256,7 @@ void prefill_kernel(PrefillArgs a) {
     const char *kb = smem + buf * 2 * kPfTileBytes;
     const char *vb = kb + kPfTileBytes;
     // S^T blocks of a 32-key half: keys key0 + 16*kb2 + (4*lg + i), columns qb.
-    auto qk = [&](int h2, f32x4 (&sc)[2][2]) {
+    auto qk = [&](int h2, f32x4 (&sc)[2][kQB]) {
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
         bf16x8 kop[D / 32];
@@ -248,7 +264,7 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int ch = 0; ch < D / 32; ++ch) kop[ch] = as_bf16x8(*reinterpret_cast<const u32x4 *>(kr + 64 * ch));
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < kQB; ++qb) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ch = 0; ch < D / 32; ++ch) acc = mfma16x16x32(kop[ch], qop[qb][ch], acc);
@@ -256,7 +272,7 @@ void prefill_kernel(PrefillArgs a) {
         }
       }
     };
-    auto softmax_pv = [&](int h2, const f32x4 (&sc)[2][2]) {
+    auto softmax_pv = [&](int h2, const f32x4 (&sc)[2][kQB]) {
       const int key0 = s * kPfBN + 32 * h2;  // position of the half's first key
       const bool diag = key0 + 31 >= q_first;  // some key may lie past some query row
       // V^T operands: lane reads V[key kappa(lg, e)][8*hl .. 8*hl+7]; step t
@@ -269,9 +285,9 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) rv[e][j] = w[j];
       }
-      bf16x8 pop[2];
+      bf16x8 pop[kQB];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+      for (int qb = 0; qb < kQB; ++qb) {
         // raw scores; scale (> 0) is applied to the max and inside the exponent
         float x[8];
 #pragma unroll
@@ -325,13 +341,13 @@ void prefill_kernel(PrefillArgs a) {
         for (int j = 0; j < 4; ++j) w[j] = pair_halves(rv[2 * j][t >> 1], rv[2 * j + 1][t >> 1], t & 1);
         const bf16x8 vop = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) o[qb][t] = mfma16x16x32(vop, pop[qb], o[qb][t]);
+        for (int qb = 0; qb < kQB; ++qb) o[qb][t] = mfma16x16x32(vop, pop[qb], o[qb][t]);
       }
     };
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {  // two 32-key halves of the stage
+    for (int h2 = 0; h2 < kHalves; ++h2) {  // 32-key steps of the stage
       if (s * kPfBN + 32 * h2 >= k_end) break;  // uniform
-      f32x4 sc[2][2];
+      f32x4 sc[2][kQB];
       qk(h2, sc);
       softmax_pv(h2, sc);
     }
@@ -346,7 +362,7 @@ void prefill_kernel(PrefillArgs a) {
 
   // Normalise and write: lane holds O[row][d = 32*lg + 8*i + t] for t = 0..7.
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < kQB; ++qb) {
     float l = l_run[qb];
     l = sum_xor16(l);
     l = sum_xor32(l);
