@@ -329,6 +329,9 @@ static int prefill_common(const char *who, const void *q, const void *k, const v
     return fail(PKV_E_SHAPE, "at most 16 query heads per KV head are supported (got %d)",
                 num_q_heads / num_kv_heads);
   if (!(scale > 0.f) || isinf(scale)) return fail(PKV_E_SHAPE, "scale must be finite and positive");
+  if ((int64_t)num_kv_heads * head_dim * 2 >= (1 << 24))  // one token's K row in bytes, a 24-bit product
+    return fail(PKV_E_SHAPE, "%s: num_kv_heads*head_dim*2 must be below 2^24 (got %d heads)", who,
+                num_kv_heads);
   if (fused) {
     int rc = check_pool(num_pages, page_size, num_kv_heads, head_dim, num_slots, max_blocks);
     if (rc) return rc;

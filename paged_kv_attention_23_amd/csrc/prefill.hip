@@ -115,6 +115,11 @@ void prefill_kernel(PrefillArgs a) {
 
   PfTile tl;
   if (!find_tile(a.cu_seqlens, a.num_docs, QT, qt_shift, tile, lane, tl)) return;  // uniform
+  tl.doc = __builtin_amdgcn_readfirstlane(tl.doc);  // uniform values: keep them in SGPRs
+  tl.doc_start = __builtin_amdgcn_readfirstlane(tl.doc_start);
+  tl.doc_end = __builtin_amdgcn_readfirstlane(tl.doc_end);
+  tl.q_lo = __builtin_amdgcn_readfirstlane(tl.q_lo);
+  tl.q_hi = __builtin_amdgcn_readfirstlane(tl.q_hi);
   // Keys are numbered by their position in the sequence: [0, prefix) are
   // cached in the pages (paged prefix, chunked prefill), [prefix, k_end) are
   // this document's packed rows, position prefix + j at packed row
@@ -173,34 +178,61 @@ void prefill_kernel(PrefillArgs a) {
   }
 
   // Cooperative stage loads: piece p = threadIdx.x + 256*i -> key row p/16, 16-byte column p%16.
+  // Keys past k_end (last stage only) are clamped to the last key: they lie
+  // past every row's position, so their scores are masked and their
+  // probabilities are exactly 0 against finite values.
   const int64_t row_stride = (int64_t)a.H_kv * D;  // elements between consecutive tokens
+  const uint32_t row_bytes = (uint32_t)row_stride * 2u;  // < 2^24, checked on the host
+  const uint32_t col_bytes = (threadIdx.x & 15) * 16u;
+  const int row0 = threadIdx.x >> 4;                    // stage row of piece 0
   const uint16_t *kg = a.k + (int64_t)g * D;
   const uint16_t *vg = a.v + (int64_t)g * D;
+  const int32_t *pt_row = kFused ? a.page_table + (int64_t)slot * a.max_blocks : nullptr;
   u32x4 stk[kPfLoads], stv[kPfLoads];
   int spage[kPfLoads];  // fused scatter: page of each piece's key (0 = skip)
   auto load_stage = [&](int s) {
+    const int key0 = s * kPfBN;  // position of the stage's first key
+    if (!kPrefix || key0 >= prefix) {
+      // This document's packed rows only: one uniform base per stage and
+      // 32-bit lane offsets.
+      const int64_t first = (int64_t)(tl.doc_start + key0 - prefix) * row_stride;
+      const char *kbs = reinterpret_cast<const char *>(kg + first);
+      const char *vbs = reinterpret_cast<const char *>(vg + first);
+      const int last = k_end - 1 - key0;  // last live row of the stage
 #pragma unroll
-    for (int i = 0; i < kPfLoads; ++i) {
-      const int p = threadIdx.x + kPfThreads * i;
-      const int pos = s * kPfBN + (p >> 4);   // key position
-      const int key = min(pos, k_end - 1);
-      if (kPrefix && key < prefix) {          // cached prefix: through the page table
-        int page = a.page_table[(int64_t)slot * a.max_blocks + (key >> a.page_shift)];
-        page = min(max(page, 0), a.num_pages - 1);
-        const int64_t row = (int64_t)g * a.plane_rows + ((int64_t)page << a.page_shift) +
-                            (key & ((1 << a.page_shift) - 1));
-        stk[i] = *reinterpret_cast<const u32x4 *>(a.k_pool + row * D + (p & 15) * 8);
-        stv[i] = *reinterpret_cast<const u32x4 *>(a.v_pool + row * D + (p & 15) * 8);
-      } else {                                // this document's packed rows
-        const int64_t off = (int64_t)(tl.doc_start + key - prefix) * row_stride + (p & 15) * 8;
-        stk[i] = *reinterpret_cast<const u32x4 *>(kg + off);
-        stv[i] = *reinterpret_cast<const u32x4 *>(vg + off);
+      for (int i = 0; i < kPfLoads; ++i) {
+        const int r = min(row0 + (kPfThreads / 16) * i, last);
+        const uint32_t off = __umul24((uint32_t)r, row_bytes) + col_bytes;
+        stk[i] = *reinterpret_cast<const u32x4 *>(kbs + off);
+        stv[i] = *reinterpret_cast<const u32x4 *>(vbs + off);
       }
-      if constexpr (kFused) {
-        spage[i] = 0;
-        const int blk = pos >> a.page_shift;
-        if (scatter && pos >= prefix && pos < k_end && blk < a.max_blocks)
-          spage[i] = a.page_table[(int64_t)slot * a.max_blocks + blk];
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPfLoads; ++i) {
+        const int p = threadIdx.x + kPfThreads * i;
+        const int key = min(key0 + (p >> 4), k_end - 1);
+        if (key < prefix) {                 // cached prefix: through the page table
+          int page = pt_row[key >> a.page_shift];
+          page = min(max(page, 0), a.num_pages - 1);
+          const int64_t row = (int64_t)g * a.plane_rows + ((int64_t)page << a.page_shift) +
+                              (key & ((1 << a.page_shift) - 1));
+          stk[i] = *reinterpret_cast<const u32x4 *>(a.k_pool + row * D + (p & 15) * 8);
+          stv[i] = *reinterpret_cast<const u32x4 *>(a.v_pool + row * D + (p & 15) * 8);
+        } else {                            // this document's packed rows
+          const int64_t off = (int64_t)(tl.doc_start + key - prefix) * row_stride + (p & 15) * 8;
+          stk[i] = *reinterpret_cast<const u32x4 *>(kg + off);
+          stv[i] = *reinterpret_cast<const u32x4 *>(vg + off);
+        }
+      }
+    }
+    if constexpr (kFused) {
+      if (scatter) {
+#pragma unroll
+        for (int i = 0; i < kPfLoads; ++i) {
+          const int pos = key0 + row0 + (kPfThreads / 16) * i;
+          const int blk = pos >> a.page_shift;
+          spage[i] = (pos >= prefix && pos < k_end && blk < a.max_blocks) ? pt_row[blk] : 0;
+        }
       }
     }
   };
@@ -217,16 +249,15 @@ void prefill_kernel(PrefillArgs a) {
       }
     }
   };
-  auto store_stage = [&](int s, int buf) {
+  auto store_stage = [&](int buf) {
     char *kb = smem + buf * 2 * kPfTileBytes;
     char *vb = kb + kPfTileBytes;
 #pragma unroll
     for (int i = 0; i < kPfLoads; ++i) {
       const int p = threadIdx.x + kPfThreads * i;
-      const bool live = s * kPfBN + (p >> 4) < k_end;
       const int off = (p >> 4) * kPfRowStride + (p & 15) * 16;
-      *reinterpret_cast<u32x4 *>(kb + off) = live ? stk[i] : u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4 *>(vb + off) = live ? stv[i] : u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4 *>(kb + off) = stk[i];
+      *reinterpret_cast<u32x4 *>(vb + off) = stv[i];
     }
   };
 
@@ -245,7 +276,7 @@ void prefill_kernel(PrefillArgs a) {
   const int nsteps = (k_end + kPfBN - 1) / kPfBN;
   const int q_first = prefix + (tl.q_lo - tl.doc_start);  // position of the tile's first row
   load_stage(0);
-  store_stage(0, 0);
+  store_stage(0);
   if constexpr (kFused) {
     if (scatter) scatter_stage(0);
   }
@@ -352,7 +383,7 @@ void prefill_kernel(PrefillArgs a) {
       softmax_pv(h2, sc);
     }
     if (s + 1 < nsteps) {
-      store_stage(s + 1, buf ^ 1);
+      store_stage(buf ^ 1);
       if constexpr (kFused) {
         if (scatter) scatter_stage(s + 1);
       }
