@@ -147,6 +147,9 @@ def test_prefill_checks(lib):
     assert f(FAKE, 0, FAKE, FAKE, 1, 10, 32, 8, 128, 0.1, FAKE, FAKE, 0) == -1
     assert f(FAKE, FAKE, FAKE, FAKE + 1, 1, 10, 32, 8, 128, 0.1, FAKE, FAKE, 0) == -3
     assert f(FAKE, FAKE, FAKE, FAKE, 1, -5, 32, 8, 128, 0.1, FAKE, FAKE, 0) == -2
+    # one token's K row (num_kv_heads*head_dim*2 bytes) must stay below 2^24
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 10, 65536, 65536, 128, 0.1, FAKE, FAKE, 0) == -2
+    assert "2^24" in B.last_error()
 
 
 def test_workspace_size(lib):
