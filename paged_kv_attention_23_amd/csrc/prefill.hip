@@ -54,6 +54,16 @@ constexpr int kPfSmem = 2 * 2 * kPfTileBytes;        // 2 stages x (K, V)
 constexpr int kPfLoads = kPfBN * (2 * kPfD / 16) / kPfThreads;  // 16-byte pieces per thread per tensor
 constexpr float kLazy = 8.f;                         // lazy-rescale threshold, log2 units
 
+// gfx950 transposing LDS read of 64 bits per lane (four 16-bit values).
+// Within each group of 16 lanes, with lane s addressing four consecutive
+// values D[s][0..3], lane i receives D[4*j + i/4][i%4] for j = 0..3.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr16(const char *p) {
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4 *)const_cast<char *>(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
 struct PfTile {
   int doc, doc_start, doc_end, q_lo, q_hi;
 };
@@ -286,6 +296,10 @@ void prefill_kernel(PrefillArgs a) {
     if (s + 1 < nsteps) load_stage(s + 1);
     const char *kb = smem + buf * 2 * kPfTileBytes;
     const char *vb = kb + kPfTileBytes;
+    // Transposing V reads: within each 16-lane group, lane hl addresses key
+    // row 4*lg + hl/4 (plus the block's first key), head_dim 32*(hl%4) + 4*t;
+    // the hardware hands lane hl the four keys' values at one head_dim.
+    const char *v_tr = vb + (4 * lg + (hl >> 2)) * kPfRowStride + 64 * (hl & 3);
     // S^T blocks of a 32-key half: keys key0 + 16*kb2 + (4*lg + i), columns qb.
     auto qk = [&](int h2, f32x4 (&sc)[2][kQB]) {
 #pragma unroll
@@ -306,16 +320,6 @@ void prefill_kernel(PrefillArgs a) {
     auto softmax_pv = [&](int h2, const f32x4 (&sc)[2][kQB]) {
       const int key0 = s * kPfBN + 32 * h2;  // position of the half's first key
       const bool diag = key0 + 31 >= q_first;  // some key may lie past some query row
-      // V^T operands: lane reads V[key kappa(lg, e)][8*hl .. 8*hl+7]; step t
-      // uses head_dim d = 8*m + t for its row m.
-      uint32_t rv[8][4];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int kr = 32 * h2 + (e < 4 ? 4 * lg + e : 16 + 4 * lg + (e - 4));
-        const u32x4 w = *reinterpret_cast<const u32x4 *>(vb + kr * kPfRowStride + 16 * hl);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) rv[e][j] = w[j];
-      }
       bf16x8 pop[kQB];
 #pragma unroll
       for (int qb = 0; qb < kQB; ++qb) {
@@ -365,12 +369,14 @@ void prefill_kernel(PrefillArgs a) {
                           pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
         pop[qb] = as_bf16x8(pw);
       }
+      // V^T operands from transposing LDS reads: lane (hl, lg) of step t
+      // gets head_dim d = 32*(hl/4) + 4*t + hl%4 at keys kappa(lg, 0..3) and
+      // kappa(lg, 4..7), the key order of P^T.
 #pragma unroll
       for (int t = 0; t < D / 16; ++t) {
-        uint32_t w[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = pair_halves(rv[2 * j][t >> 1], rv[2 * j + 1][t >> 1], t & 1);
-        const bf16x8 vop = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
+        const u32x2 lo = lds_read_tr16(v_tr + (32 * h2) * kPfRowStride + 8 * t);
+        const u32x2 hi = lds_read_tr16(v_tr + (32 * h2 + 16) * kPfRowStride + 8 * t);
+        const bf16x8 vop = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb) o[qb][t] = mfma16x16x32(vop, pop[qb], o[qb][t]);
       }
@@ -391,7 +397,7 @@ void prefill_kernel(PrefillArgs a) {
     __syncthreads();
   }
 
-  // Normalise and write: lane holds O[row][d = 32*lg + 8*i + t] for t = 0..7.
+  // Normalise and write: lane holds O[row][d = 32*lg + 4*t + i] in o[qb][t][i].
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
     float l = l_run[qb];
@@ -402,12 +408,11 @@ void prefill_kernel(PrefillArgs a) {
     const int64_t rh = (int64_t)col_q[qb] * a.H_q + col_head[qb];
     uint16_t *orow = a.out + rh * D + 32 * lg;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const u32x4 w = {pack_bf16x2(o[qb][0][i] * inv, o[qb][1][i] * inv),
-                       pack_bf16x2(o[qb][2][i] * inv, o[qb][3][i] * inv),
-                       pack_bf16x2(o[qb][4][i] * inv, o[qb][5][i] * inv),
-                       pack_bf16x2(o[qb][6][i] * inv, o[qb][7][i] * inv)};
-      *reinterpret_cast<u32x4 *>(orow + 8 * i) = w;
+    for (int c = 0; c < 4; ++c) {  // 16-byte piece c: d = 32*lg + 8*c + 0..7 = steps 2c, 2c+1
+      const f32x4 a0 = o[qb][2 * c], a1 = o[qb][2 * c + 1];
+      const u32x4 w = {pack_bf16x2(a0[0] * inv, a0[1] * inv), pack_bf16x2(a0[2] * inv, a0[3] * inv),
+                       pack_bf16x2(a1[0] * inv, a1[1] * inv), pack_bf16x2(a1[2] * inv, a1[3] * inv)};
+      *reinterpret_cast<u32x4 *>(orow + 8 * c) = w;
     }
     if (lg == 0) a.lse[rh] = (l > 0.f) ? (m_run[qb] + log2f(l)) * kLn2 : -INFINITY;
   }
