@@ -198,11 +198,36 @@ void prefill_kernel(PrefillArgs a) {
   const uint16_t *kg = a.k + (int64_t)g * D;
   const uint16_t *vg = a.v + (int64_t)g * D;
   const int32_t *pt_row = kFused ? a.page_table + (int64_t)slot * a.max_blocks : nullptr;
+  // Cached prefix: page ids of the document's first 64 blocks, one per lane,
+  // loaded once.  A stage inside the prefix lies within one page when pages
+  // hold at least a stage of keys (stages start at multiples of kPfBN), so it
+  // needs one page id (a lane read) and one uniform base.
+  const bool stage_in_page = (1 << a.page_shift) >= kPfBN;
+  int pwin = 0;
+  if constexpr (kPrefix) {
+    const int nblk = (prefix + (1 << a.page_shift) - 1) >> a.page_shift;
+    if (lane < nblk && lane < a.max_blocks) pwin = pt_row[lane];
+  }
   u32x4 stk[kPfLoads], stv[kPfLoads];
   int spage[kPfLoads];  // fused scatter: page of each piece's key (0 = skip)
   auto load_stage = [&](int s) {
     const int key0 = s * kPfBN;  // position of the stage's first key
-    if (!kPrefix || key0 >= prefix) {
+    if (kPrefix && stage_in_page && key0 + kPfBN <= prefix) {
+      // Whole stage in one cached page.
+      const int blk = key0 >> a.page_shift;
+      int page = blk < kWave ? __builtin_amdgcn_readlane(pwin, blk) : pt_row[blk];
+      page = min(max(page, 0), a.num_pages - 1);
+      const int64_t first = ((int64_t)g * a.plane_rows + ((int64_t)page << a.page_shift) +
+                             (key0 & ((1 << a.page_shift) - 1))) * D;
+      const char *kbs = reinterpret_cast<const char *>(a.k_pool + first);
+      const char *vbs = reinterpret_cast<const char *>(a.v_pool + first);
+#pragma unroll
+      for (int i = 0; i < kPfLoads; ++i) {
+        const uint32_t off = (uint32_t)(row0 + (kPfThreads / 16) * i) * (uint32_t)(D * 2) + col_bytes;
+        stk[i] = *reinterpret_cast<const u32x4 *>(kbs + off);
+        stv[i] = *reinterpret_cast<const u32x4 *>(vbs + off);
+      }
+    } else if (!kPrefix || key0 >= prefix) {
       // This document's packed rows only: one uniform base per stage and
       // 32-bit lane offsets.
       const int64_t first = (int64_t)(tl.doc_start + key0 - prefix) * row_stride;

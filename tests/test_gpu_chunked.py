@@ -47,6 +47,9 @@ CASES = [
     (95, [2000], [1], 32, 8, 128, None),                                    # decode-like chunk
     (96, [int(x) for x in np.random.default_rng(96).integers(0, 400, 70)],
      [int(x) for x in np.random.default_rng(97).integers(1, 40, 70)], 32, 8, 16, None),  # 70 seqs
+    # prefixes past 64 pages of 64 tokens (page ids beyond the per-tile window of 64)
+    (99, [4700, 4160, 4096, 4095], [40, 64, 3, 1], 16, 2, 64, None),
+    (100, [700, 257, 256, 255], [33, 100, 1, 64], 32, 8, 256, None),        # page_size 256
 ]
 
 
