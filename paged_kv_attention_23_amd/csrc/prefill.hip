@@ -52,6 +52,7 @@ constexpr int kPfRowStride = 2 * kPfD + 16;          // bytes per key row in LDS
 constexpr int kPfTileBytes = kPfBN * kPfRowStride;   // one K or V stage
 constexpr int kPfSmem = 2 * 2 * kPfTileBytes;        // 2 stages x (K, V)
 constexpr int kPfLoads = kPfBN * (2 * kPfD / 16) / kPfThreads;  // 16-byte pieces per thread per tensor
+static_assert(kPfThreads / 16 == 16, "a stage piece spans 16 keys, the smallest page");
 constexpr float kLazy = 8.f;                         // lazy-rescale threshold, log2 units
 
 // gfx950 transposing LDS read of 64 bits per lane (four 16-bit values).
@@ -199,10 +200,10 @@ void prefill_kernel(PrefillArgs a) {
   const uint16_t *vg = a.v + (int64_t)g * D;
   const int32_t *pt_row = kFused ? a.page_table + (int64_t)slot * a.max_blocks : nullptr;
   // Cached prefix: page ids of the document's first 64 blocks, one per lane,
-  // loaded once.  A stage inside the prefix lies within one page when pages
-  // hold at least a stage of keys (stages start at multiples of kPfBN), so it
-  // needs one page id (a lane read) and one uniform base.
-  const bool stage_in_page = (1 << a.page_shift) >= kPfBN;
+  // loaded once.  In a stage inside the prefix, piece i covers the 16 keys
+  // key0 + 16*i .. +15, which lie in one page (pages hold >= 16 keys and the
+  // pieces are 16-aligned), so each piece needs one page id (a lane read)
+  // and one uniform base.
   int pwin = 0;
   if constexpr (kPrefix) {
     const int nblk = (prefix + (1 << a.page_shift) - 1) >> a.page_shift;
@@ -212,20 +213,19 @@ void prefill_kernel(PrefillArgs a) {
   int spage[kPfLoads];  // fused scatter: page of each piece's key (0 = skip)
   auto load_stage = [&](int s) {
     const int key0 = s * kPfBN;  // position of the stage's first key
-    if (kPrefix && stage_in_page && key0 + kPfBN <= prefix) {
-      // Whole stage in one cached page.
-      const int blk = key0 >> a.page_shift;
-      int page = blk < kWave ? __builtin_amdgcn_readlane(pwin, blk) : pt_row[blk];
-      page = min(max(page, 0), a.num_pages - 1);
-      const int64_t first = ((int64_t)g * a.plane_rows + ((int64_t)page << a.page_shift) +
-                             (key0 & ((1 << a.page_shift) - 1))) * D;
-      const char *kbs = reinterpret_cast<const char *>(a.k_pool + first);
-      const char *vbs = reinterpret_cast<const char *>(a.v_pool + first);
+    if (kPrefix && key0 + kPfBN <= prefix) {
+      // Whole stage in the cached prefix: one page per 16-key piece.
+      const uint32_t off = (uint32_t)row0 * (uint32_t)(D * 2) + col_bytes;
 #pragma unroll
       for (int i = 0; i < kPfLoads; ++i) {
-        const uint32_t off = (uint32_t)(row0 + (kPfThreads / 16) * i) * (uint32_t)(D * 2) + col_bytes;
-        stk[i] = *reinterpret_cast<const u32x4 *>(kbs + off);
-        stv[i] = *reinterpret_cast<const u32x4 *>(vbs + off);
+        const int key = key0 + (kPfThreads / 16) * i;  // the piece's first key
+        const int blk = key >> a.page_shift;
+        int page = blk < kWave ? __builtin_amdgcn_readlane(pwin, blk) : pt_row[blk];
+        page = min(max(page, 0), a.num_pages - 1);
+        const int64_t first = ((int64_t)g * a.plane_rows + ((int64_t)page << a.page_shift) +
+                               (key & ((1 << a.page_shift) - 1))) * D;
+        stk[i] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(a.k_pool + first) + off);
+        stv[i] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(a.v_pool + first) + off);
       }
     } else if (!kPrefix || key0 >= prefix) {
       // This document's packed rows only: one uniform base per stage and
