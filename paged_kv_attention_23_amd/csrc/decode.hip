@@ -36,9 +36,8 @@ constexpr int kTileKeys = 32;
 
 template <int D>
 struct DecGeom {
-  static constexpr int kRowBytes = 2 * D;
-  static constexpr int kChunkBytes = 4 * kRowBytes + 32;  // 4 key rows, then 32 B of padding
-  static constexpr int kVBytes = (kTileKeys / 4) * kChunkBytes;  // one wave's V tile
+  static constexpr int kRowStride = 2 * D + 16;  // bytes per key row in a wave's V tile
+  static constexpr int kVBytes = kTileKeys * kRowStride;  // one wave's V tile
   static constexpr int kDChunks = D / 32;    // QK steps over head_dim
   static constexpr int kDBlocks = D / 16;    // PV output blocks over head_dim
   static constexpr int kVLoads = D / 16;     // 16-byte V loads per lane per tile
@@ -125,8 +124,7 @@ __device__ __forceinline__ void store_v(const u32x4 (&v)[D / 16], char *vlds, in
     const int key = i * Gm::kKeysPerLoad + lane / Gm::kLanesPerRow;
     u32x4 val = v[i];
     if (tail && kt + key >= hi) val = u32x4{0u, 0u, 0u, 0u};
-    const int off = (key >> 2) * Gm::kChunkBytes + (key & 3) * Gm::kRowBytes +
-                    (lane % Gm::kLanesPerRow) * 16;
+    const int off = key * Gm::kRowStride + (lane % Gm::kLanesPerRow) * 16;
     *reinterpret_cast<u32x4 *>(vlds + off) = val;
   }
 }
@@ -188,38 +186,20 @@ __device__ __forceinline__ void compute_tile(const u32x4 (&k)[2][D / 32], int kt
                     pack_bf16x2(p[6], p[7])};
   const bf16x8 pop = as_bf16x8(pw);
 
-  // 4) O^T += V^T P^T.  PV step t uses V^T rows d(t, m) = NT*m + t
-  //    (NT = D/16 steps): lane (hl, lg) reads the NT consecutive values
-  //    V[key][NT*hl .. NT*hl+NT-1] once per key kappa(lg, e) and feeds every
-  //    step from them.  Accumulator (t, i) of lane (hl, lg) is therefore
-  //    O[head hl][NT*(4*lg+i) + t].
+  // 4) O^T += V^T P^T with V^T operands from transposing LDS reads.  In
+  //    each 16-lane group, lane hl addresses key row 4*lg + hl/4 (plus 16
+  //    for the second read) at head_dim 4*NT*(hl%4) + 4*t, and receives one
+  //    head_dim value at four consecutive keys: step t's A-operand row hl is
+  //    d = 4*NT*(hl/4) + 4*t + hl%4, keys kappa(lg, 0..7) in P^T's order.
+  //    Accumulator (t, i) of lane (hl, lg) is therefore
+  //    O[head hl][4*NT*lg + 4*t + i].
   constexpr int NT = Gm::kDBlocks;
-  constexpr int NW = NT / 2;  // 32-bit words per lane per key
-  uint32_t rv[8][NW];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int key = e < 4 ? 4 * lg + e : 16 + 4 * lg + (e - 4);
-    const char *src = vlds + (key >> 2) * Gm::kChunkBytes + (key & 3) * Gm::kRowBytes + 2 * NT * hl;
-    if constexpr (NW == 4) {
-      const u32x4 w = *reinterpret_cast<const u32x4 *>(src);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) rv[e][j] = w[j];
-    } else {
-      const u32x2 w = *reinterpret_cast<const u32x2 *>(src);
-#pragma unroll
-      for (int j = 0; j < NW; ++j) rv[e][j] = w[j];
-    }
-  }
+  const char *v_tr = vlds + (4 * lg + (hl >> 2)) * Gm::kRowStride + 8 * NT * (hl & 3);
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    uint32_t w[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t a0 = rv[2 * j][t >> 1], a1 = rv[2 * j + 1][t >> 1];
-      w[j] = pair_halves(a0, a1, t & 1);
-    }
-    const u32x4 vw = {w[0], w[1], w[2], w[3]};
-    o[t] = mfma16x16x32(as_bf16x8(vw), pop, o[t]);
+    const u32x2 lo = lds_read_tr16(v_tr + 8 * t);
+    const u32x2 hi = lds_read_tr16(v_tr + 16 * Gm::kRowStride + 8 * t);
+    o[t] = mfma16x16x32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pop, o[t]);
   }
 }
 
@@ -418,7 +398,7 @@ __device__ void decode_piece(const DecodeArgs &a, char *smem, int r, int g, int 
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const int k = NT * i + t;  // element of this lane's D/4 new-V values
+        const int k = 4 * t + i;  // element of this lane's D/4 new-V values
         const uint32_t w = vq[k >> 3][(k >> 1) & 3];
         o[t][i] = o[t][i] * alpha + pn * ((k & 1) ? bf16_hi(w) : bf16_lo(w));
       }
@@ -434,11 +414,9 @@ __device__ void decode_piece(const DecodeArgs &a, char *smem, int r, int g, int 
   float *mm = mo + kDecWaves * 16 * D;                // [wave][16]
   float *ml = mm + kDecWaves * 16;                    // [wave][16]
   if (hl < G) {
-    constexpr int NT = Gm::kDBlocks;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int tt = 0; tt < NT; ++tt) mo[(wave * 16 + hl) * D + NT * (4 * lg + i) + tt] = o[tt][i];
+    for (int tt = 0; tt < NT; ++tt)
+      *reinterpret_cast<f32x4 *>(mo + (wave * 16 + hl) * D + 4 * NT * lg + 4 * tt) = o[tt];
     if (lg == 0) {
       mm[wave * 16 + hl] = m_run;
       ml[wave * 16 + hl] = l_run;

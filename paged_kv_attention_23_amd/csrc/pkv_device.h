@@ -63,12 +63,17 @@ __device__ __forceinline__ float sum_xor32(float v) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// Pair the low (hi = false) or high (hi = true) bf16 halves of two words:
-// result = {a0.half, a1.half} (a0's half in the low 16 bits), one v_perm_b32.
-// v_perm_b32 selector bytes 0-3 pick bytes of its second source, 4-7 bytes of
-// its first source.
-__device__ __forceinline__ uint32_t pair_halves(uint32_t a0, uint32_t a1, bool hi) {
-  return __builtin_amdgcn_perm(a1, a0, hi ? 0x07060302u : 0x05040100u);
+// gfx950 transposing LDS read of 64 bits per lane (four 16-bit values).
+// Within each group of 16 lanes, with lane s addressing four consecutive
+// values D[s][0..3], lane i receives D[4*j + i/4][i%4] for j = 0..3: if lane s
+// addresses key row k0 + s/4 at column c(s%4), lane i receives column
+// c(i/4) + i%4 of the four rows k0..k0+3, a column operand for the matrix
+// cores.  The address must be 8-byte aligned.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr16(const char *p) {
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4 *)const_cast<char *>(p));
+  return __builtin_bit_cast(u32x2, r);
 }
 
 }  // namespace pkv

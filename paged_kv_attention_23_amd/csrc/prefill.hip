@@ -55,16 +55,6 @@ constexpr int kPfLoads = kPfBN * (2 * kPfD / 16) / kPfThreads;  // 16-byte piece
 static_assert(kPfThreads / 16 == 16, "a stage piece spans 16 keys, the smallest page");
 constexpr float kLazy = 8.f;                         // lazy-rescale threshold, log2 units
 
-// gfx950 transposing LDS read of 64 bits per lane (four 16-bit values).
-// Within each group of 16 lanes, with lane s addressing four consecutive
-// values D[s][0..3], lane i receives D[4*j + i/4][i%4] for j = 0..3.
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ u32x2 lds_read_tr16(const char *p) {
-  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) i16x4 *)const_cast<char *>(p));
-  return __builtin_bit_cast(u32x2, r);
-}
-
 struct PfTile {
   int doc, doc_start, doc_end, q_lo, q_hi;
 };
