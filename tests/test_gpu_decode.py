@@ -219,6 +219,7 @@ SMALL = [
     (34, 12, 4, 64, 16, [5, 96, 33, 1000], "sequential"),                    # G = 3
     (35, 32, 8, 128, 256, [255, 256, 257, 2048], "shuffled"),                # big pages
     (36, 32, 8, 128, 16, [16 * 40, 16 * 40 - 1, 16 * 70 + 3], "shuffled"),   # > 64 blocks
+    (37, 32, 8, 128, 128, [32768, 20001, 8193], "shuffled"),                 # long contexts
 ]
 
 

@@ -75,6 +75,7 @@ SMALL = [
     (64, 32, 8, 128, 16, [16 * 40, 16 * 70 + 3, 33], None),             # > 64 blocks
     (65, 32, 8, 128, 128, [700, 1, 0, 513] * 4,
      [0 if i % 4 == 1 else i + 1 for i in range(16)]),                  # padding rows
+    (66, 32, 8, 128, 128, [32768, 20001, 8193], None),                  # long contexts
 ]
 
 
