@@ -638,11 +638,22 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(DecodeArgs a) {
   const int64_t nrh = (int64_t)a.B * a.H_q;
   if (rh >= nrh) return;
   const int S = a.num_splits;
+  constexpr int kPer = D / kWave;  // elements of head_dim per lane
+  // The first kPre splits' partials are loaded together with the LSEs (they
+  // do not depend on the weights), so the merge waits for one memory round
+  // trip rather than two.
+  constexpr int kPre = 8;
+  float pre[kPre][kPer];
+#pragma unroll
+  for (int s = 0; s < kPre; ++s) {
+    const float *op = a.o_part + ((int64_t)s * nrh + rh) * D + lane * kPer;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) pre[s][k] = (s < S) ? op[k] : 0.f;
+  }
   const float ls = (lane < S) ? a.lse_part[(int64_t)lane * nrh + rh] : -INFINITY;
   float M = ls;
 #pragma unroll
   for (int m = 1; m < kWave; m <<= 1) M = fmaxf(M, shfl_xor_f(M, m));
-  constexpr int kPer = D / kWave;  // elements of head_dim per lane
   if (M == -INFINITY) {
 #pragma unroll
     for (int k = 0; k < kPer; ++k) a.out[rh * D + lane * kPer + k] = 0;
@@ -658,7 +669,14 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(DecodeArgs a) {
   float acc[kPer];
 #pragma unroll
   for (int k = 0; k < kPer; ++k) acc[k] = 0.f;
-  for (int s = 0; s < S; ++s) {
+#pragma unroll
+  for (int s = 0; s < kPre; ++s) {
+    const float ws = __shfl(w, s, kWave);
+    if (s >= S || ws == 0.f) continue;  // uniform: every lane sees the same ws
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) acc[k] += ws * pre[s][k];
+  }
+  for (int s = kPre; s < S; ++s) {
     const float ws = __shfl(w, s, kWave);
     if (ws == 0.f) continue;  // uniform: every lane sees the same ws
     const float *op = a.o_part + ((int64_t)s * nrh + rh) * D + lane * kPer;
