@@ -335,7 +335,18 @@ void prefill_kernel(PrefillArgs a) {
     auto softmax_pv = [&](int h2, const f32x4 (&sc)[2][kQB]) {
       const int key0 = s * kPfBN + 32 * h2;  // position of the half's first key
       const bool diag = key0 + 31 >= q_first;  // some key may lie past some query row
-      bf16x8 pop[kQB];
+      // V^T operands from transposing LDS reads: lane (hl, lg) of step t
+      // gets head_dim d = 32*(hl/4) + 4*t + hl%4 at keys kappa(lg, 0..3) and
+      // kappa(lg, 4..7), the key order of P^T.  All eight are read first, so
+      // that a column block's PV products can be issued as soon as its
+      // softmax is done and run on the matrix cores during the next block's.
+      bf16x8 vop[D / 16];
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) {
+        const u32x2 lo = lds_read_tr16(v_tr + (32 * h2) * kPfRowStride + 8 * t);
+        const u32x2 hi = lds_read_tr16(v_tr + (32 * h2 + 16) * kPfRowStride + 8 * t);
+        vop[t] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+      }
 #pragma unroll
       for (int qb = 0; qb < kQB; ++qb) {
         // raw scores; scale (> 0) is applied to the max and inside the exponent
@@ -382,18 +393,9 @@ void prefill_kernel(PrefillArgs a) {
         l_run[qb] += ps;
         const u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                           pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-        pop[qb] = as_bf16x8(pw);
-      }
-      // V^T operands from transposing LDS reads: lane (hl, lg) of step t
-      // gets head_dim d = 32*(hl/4) + 4*t + hl%4 at keys kappa(lg, 0..3) and
-      // kappa(lg, 4..7), the key order of P^T.
+        const bf16x8 pop = as_bf16x8(pw);
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t) {
-        const u32x2 lo = lds_read_tr16(v_tr + (32 * h2) * kPfRowStride + 8 * t);
-        const u32x2 hi = lds_read_tr16(v_tr + (32 * h2 + 16) * kPfRowStride + 8 * t);
-        const bf16x8 vop = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-#pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) o[qb][t] = mfma16x16x32(vop, pop[qb], o[qb][t]);
+        for (int t = 0; t < D / 16; ++t) o[qb][t] = mfma16x16x32(vop[t], pop, o[qb][t]);
       }
     };
 #pragma unroll
