@@ -11,7 +11,7 @@ from workloads import BF16_NAN, make_case, make_decode_case
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
-if not torch.cuda.is_available():  # pragma: no cover - GPU tests only run on the GPU machine
+if not torch.cuda.is_available():  # pragma: no cover - these tests need a GPU
     pytest.skip("no GPU", allow_module_level=True)
 
 import paged_kv_attention_23_amd as pkv  # noqa: E402
