@@ -15,9 +15,9 @@
 //  * Online softmax in base 2 in fp32 registers: each lane owns one head and
 //    eight keys of the tile; the tile max needs two cross-row shuffles.
 //  * O^T[d][head] += V^T P^T on the matrix core.  The score layout already is
-//    the B operand P^T (key order permuted consistently); V^T is read from a
-//    per-wave LDS tile whose 4-key chunks are padded so the transposed reads
-//    hit distinct banks.
+//    the B operand P^T (key order permuted consistently); V^T comes from a
+//    per-wave LDS tile through gfx950's transposing LDS reads, its key rows
+//    padded so those reads hit distinct banks.
 //  * The contiguous fast path (flex_vs_vllm.md page, option table: blocks
 //    are contiguous) replaces per-block page-table lookups with one linear
 //    row base when a unit's pages are consecutive ids.

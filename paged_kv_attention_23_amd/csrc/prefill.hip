@@ -18,11 +18,11 @@
 //  * Each of the 4 waves owns 32 of the 128 rows (two 16-column blocks).
 //    Scores are computed transposed, S^T[key][row] = K Q^T, so the score
 //    layout is directly the B operand P^T of O^T = V^T P^T (the same scheme
-//    as the decode kernel); V^T operands come from 16-byte LDS reads of V
-//    rows, with the head_dim order permuted consistently.
+//    as the decode kernel); V^T operands come from gfx950's transposing LDS
+//    reads, which hand each lane one head_dim value at four keys.
 //  * K/V stages of 64 keys are double buffered in LDS (row stride padded by
-//    16 bytes so both the K-operand and V reads spread over all banks); the
-//    next stage's global loads are in flight while the current one is used.
+//    16 bytes against bank conflicts); the next stage's global loads are in
+//    flight while the current one is used.
 //  * Online softmax in base 2 in fp32; causal masking only on stages that
 //    reach the diagonal.
 #include <math.h>
