@@ -372,6 +372,8 @@ def main():
         flops = pc.flops()
         pa_ms, pre_ms = pa_total / K, pre_total / K
         tflops = flops / (pa_ms * 1e-3) / 1e12
+        p_bytes = (pc.L * (pc.H_q + 2 * pc.H_kv) * pc.D * 2 + pc.L * pc.H_q * pc.D * 2
+                   + pc.L * pc.H_q * 4)
         out["prefill"] = {
             "workload": "packed prefill, 64 prompts U[64,512] (L=%d), H_q=32 H_kv=8 D=128, "
                         "document-causal, + append into shuffled 128-token pages" % pc.L,
@@ -390,6 +392,10 @@ def main():
                 "unit": "TFLOP/s",
                 "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
                 "traffic": measured_traffic("prefill", "prefill.hip"),
+                # the same call against HBM: q, k, v read once, out and lse written once
+                "compulsory_bytes": int(p_bytes),
+                "hbm_achieved_gbs": round(p_bytes / (pa_ms * 1e-3) / 1e9, 2),
+                "hbm_frac": round(p_bytes / (pa_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             },
             "cache": f"cold: {prefill['layers']} input sets read round-robin",
         }
