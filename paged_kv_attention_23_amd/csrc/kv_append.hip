@@ -41,7 +41,9 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendArgs a,
     const int piece = r & ((1 << row_shift) - 1);
     const uint16_t *src = (is_v ? a.v_new : a.k_new) + (t * a.H_kv + h) * a.D + piece * 8;
     uint16_t *dst = (is_v ? a.v_pool : a.k_pool) + ((int64_t)h * a.plane_rows + row) * a.D + piece * 8;
-    *reinterpret_cast<u32x4 *>(dst) = *reinterpret_cast<const u32x4 *>(src);
+    // Each byte is read once and written once: stream it past the caches.
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src));
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst));
   }
 }
 
