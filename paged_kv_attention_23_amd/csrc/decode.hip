@@ -83,7 +83,8 @@ __device__ __forceinline__ uint32_t block_row(const RowCtx &c, int key0) {
 }
 
 // K rows of a 32-key tile as QK A-operands.  kbase is the KV head's plane;
-// offsets are 32-bit (a head plane is below 4 GiB).
+// offsets are 32-bit (a head plane is below 4 GiB).  K and V are streamed
+// once per call, so their loads are non-temporal.
 template <int D>
 __device__ __forceinline__ void load_k(u32x4 (&k)[2][D / 32], const RowCtx &c, const char *kbase,
                                        int kt, int lane) {
@@ -93,7 +94,7 @@ __device__ __forceinline__ void load_k(u32x4 (&k)[2][D / 32], const RowCtx &c, c
     const uint32_t off = (block_row(c, kt + 16 * b) + hl) * (2u * D) + 16u * lg;
 #pragma unroll
     for (int ch = 0; ch < D / 32; ++ch)
-      k[b][ch] = *reinterpret_cast<const u32x4 *>(kbase + off + 64u * ch);
+      k[b][ch] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kbase + off + 64u * ch));
   }
 }
 
@@ -108,7 +109,8 @@ __device__ __forceinline__ void load_v(u32x4 (&v)[D / 16], const RowCtx &c, cons
   for (int i = 0; i < Gm::kVLoads; ++i) {
     const int first = i * Gm::kKeysPerLoad;                 // first key of this load in the tile
     const uint32_t rb = (first < 16) ? row0 : row1;         // a load never straddles blocks
-    v[i] = *reinterpret_cast<const u32x4 *>(vbase + (rb + (first & 15)) * (2u * D) + lane_off);
+    v[i] = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4 *>(vbase + (rb + (first & 15)) * (2u * D) + lane_off));
   }
 }
 
