@@ -269,8 +269,9 @@ void prefill_kernel(PrefillArgs a) {
         const int pos = s * kPfBN + (p >> 4);
         const int64_t row = (int64_t)g * a.plane_rows + ((int64_t)spage[i] << a.page_shift) +
                             (pos & ((1 << a.page_shift) - 1));
-        *reinterpret_cast<u32x4 *>(a.k_pool + row * D + (p & 15) * 8) = stk[i];
-        *reinterpret_cast<u32x4 *>(a.v_pool + row * D + (p & 15) * 8) = stv[i];
+        // whole 256-byte rows, not read again here: past the caches
+        __builtin_nontemporal_store(stk[i], reinterpret_cast<u32x4 *>(a.k_pool + row * D + (p & 15) * 8));
+        __builtin_nontemporal_store(stv[i], reinterpret_cast<u32x4 *>(a.v_pool + row * D + (p & 15) * 8));
       }
     }
   };
