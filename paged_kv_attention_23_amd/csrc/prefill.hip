@@ -48,9 +48,11 @@ constexpr int kQB = PKV_PF_QB;                       // 16-column blocks per wav
 constexpr int kPfRows = 16 * kQB * kPfWaves;         // (head, query) rows per workgroup
 constexpr int kPfBN = PKV_PF_BN;                     // keys per LDS stage (multiple of 32)
 constexpr int kHalves = kPfBN / 32;                  // 32-key steps per stage
-constexpr int kPfRowStride = 2 * kPfD + 16;          // bytes per key row in LDS
-constexpr int kPfTileBytes = kPfBN * kPfRowStride;   // one K or V stage
-constexpr int kPfSmem = 2 * 2 * kPfTileBytes;        // 2 stages x (K, V)
+constexpr int kPfRowStride = 2 * kPfD + 16;          // bytes per K row in LDS
+constexpr int kPfVRowStride = 2 * kPfD + 64;         // bytes per V row in LDS
+constexpr int kPfKTileBytes = kPfBN * kPfRowStride;  // one K stage
+constexpr int kPfStageBytes = kPfKTileBytes + kPfBN * kPfVRowStride;  // K, then V
+constexpr int kPfSmem = 2 * kPfStageBytes;           // 2 stages
 constexpr int kPfLoads = kPfBN * (2 * kPfD / 16) / kPfThreads;  // 16-byte pieces per thread per tensor
 static_assert(kPfThreads / 16 == 16, "a stage piece spans 16 keys, the smallest page");
 constexpr float kLazy = 8.f;                         // lazy-rescale threshold, log2 units
@@ -276,14 +278,13 @@ void prefill_kernel(PrefillArgs a) {
     }
   };
   auto store_stage = [&](int buf) {
-    char *kb = smem + buf * 2 * kPfTileBytes;
-    char *vb = kb + kPfTileBytes;
+    char *kb = smem + buf * kPfStageBytes;
+    char *vb = kb + kPfKTileBytes;
 #pragma unroll
     for (int i = 0; i < kPfLoads; ++i) {
       const int p = threadIdx.x + kPfThreads * i;
-      const int off = (p >> 4) * kPfRowStride + (p & 15) * 16;
-      *reinterpret_cast<u32x4 *>(kb + off) = stk[i];
-      *reinterpret_cast<u32x4 *>(vb + off) = stv[i];
+      *reinterpret_cast<u32x4 *>(kb + (p >> 4) * kPfRowStride + (p & 15) * 16) = stk[i];
+      *reinterpret_cast<u32x4 *>(vb + (p >> 4) * kPfVRowStride + (p & 15) * 16) = stv[i];
     }
   };
 
@@ -310,12 +311,14 @@ void prefill_kernel(PrefillArgs a) {
   for (int s = 0; s < nsteps; ++s) {
     const int buf = s & 1;
     if (s + 1 < nsteps) load_stage(s + 1);
-    const char *kb = smem + buf * 2 * kPfTileBytes;
-    const char *vb = kb + kPfTileBytes;
+    const char *kb = smem + buf * kPfStageBytes;
+    const char *vb = kb + kPfKTileBytes;
     // Transposing V reads: within each 16-lane group, lane hl addresses key
-    // row 4*lg + hl/4 (plus the block's first key), head_dim 32*(hl%4) + 4*t;
-    // the hardware hands lane hl the four keys' values at one head_dim.
-    const char *v_tr = vb + (4 * lg + (hl >> 2)) * kPfRowStride + 64 * (hl & 3);
+    // row 4*lg + hl/4 (plus the block's first key) at head_dim
+    // 32*(t/2) + 8*(hl%4) + 4*(t%2); the hardware hands lane hl the four
+    // keys' values at one head_dim.  (V rows are 320 bytes apart, so the 16
+    // addresses of a group fall in distinct banks.)
+    const char *v_tr = vb + (4 * lg + (hl >> 2)) * kPfVRowStride + 16 * (hl & 3);
     // S^T blocks of a 32-key half: keys key0 + 16*kb2 + (4*lg + i), columns qb.
     auto qk = [&](int h2, f32x4 (&sc)[2][kQB]) {
 #pragma unroll
@@ -337,15 +340,16 @@ void prefill_kernel(PrefillArgs a) {
       const int key0 = s * kPfBN + 32 * h2;  // position of the half's first key
       const bool diag = key0 + 31 >= q_first;  // some key may lie past some query row
       // V^T operands from transposing LDS reads: lane (hl, lg) of step t
-      // gets head_dim d = 32*(hl/4) + 4*t + hl%4 at keys kappa(lg, 0..3) and
-      // kappa(lg, 4..7), the key order of P^T.  All eight are read first, so
+      // gets head_dim d = 32*(t/2) + 8*(hl/4) + 4*(t%2) + hl%4 at keys
+      // kappa(lg, 0..3) and kappa(lg, 4..7), the key order of P^T.  All eight are read first, so
       // that a column block's PV products can be issued as soon as its
       // softmax is done and run on the matrix cores during the next block's.
       bf16x8 vop[D / 16];
 #pragma unroll
       for (int t = 0; t < D / 16; ++t) {
-        const u32x2 lo = lds_read_tr16(v_tr + (32 * h2) * kPfRowStride + 8 * t);
-        const u32x2 hi = lds_read_tr16(v_tr + (32 * h2 + 16) * kPfRowStride + 8 * t);
+        const int col = 64 * (t >> 1) + 8 * (t & 1);  // bytes: head_dim 32*(t/2) + 4*(t%2)
+        const u32x2 lo = lds_read_tr16(v_tr + (32 * h2) * kPfVRowStride + col);
+        const u32x2 hi = lds_read_tr16(v_tr + (32 * h2 + 16) * kPfVRowStride + col);
         vop[t] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
       }
 #pragma unroll
@@ -415,7 +419,9 @@ void prefill_kernel(PrefillArgs a) {
     __syncthreads();
   }
 
-  // Normalise and write: lane holds O[row][d = 32*lg + 4*t + i] in o[qb][t][i].
+  // Normalise and write: lane holds O[row][d = 32*(t/2) + 8*lg + 4*(t%2) + i]
+  // in o[qb][t][i], so steps 2c and 2c+1 are 8 contiguous values and the four
+  // lanes of a row write 64 contiguous bytes per store.
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
     float l = l_run[qb];
@@ -424,13 +430,13 @@ void prefill_kernel(PrefillArgs a) {
     if (!col_ok[qb]) continue;
     const float inv = (l > 0.f) ? 1.f / l : 0.f;
     const int64_t rh = (int64_t)col_q[qb] * a.H_q + col_head[qb];
-    uint16_t *orow = a.out + rh * D + 32 * lg;
+    uint16_t *orow = a.out + rh * D + 8 * lg;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {  // 16-byte piece c: d = 32*lg + 8*c + 0..7 = steps 2c, 2c+1
+    for (int c = 0; c < 4; ++c) {  // 16-byte piece c: d = 32*c + 8*lg + 0..7 = steps 2c, 2c+1
       const f32x4 a0 = o[qb][2 * c], a1 = o[qb][2 * c + 1];
       const u32x4 w = {pack_bf16x2(a0[0] * inv, a0[1] * inv), pack_bf16x2(a0[2] * inv, a0[3] * inv),
                        pack_bf16x2(a1[0] * inv, a1[1] * inv), pack_bf16x2(a1[2] * inv, a1[3] * inv)};
-      *reinterpret_cast<u32x4 *>(orow + 8 * c) = w;
+      *reinterpret_cast<u32x4 *>(orow + 32 * c) = w;
     }
     if (lg == 0) a.lse[rh] = (l > 0.f) ? (m_run[qb] + log2f(l)) * kLn2 : -INFINITY;
   }
