@@ -79,8 +79,9 @@ int paged_kv_append(void *k_pool, void *v_pool, int32_t num_pages, int32_t page_
 /*
  * paged_decode_workspace_size - bytes of workspace paged_decode_attn needs
  * for these num_splits and flags (the same values as in the call).  For
- * num_splits == 0 without PKV_F_BALANCED it covers the largest split count
- * the automatic choice can make for this batch; with PKV_F_BALANCED it
+ * num_splits == 0 without PKV_F_BALANCED it covers both automatic choices
+ * (the largest per-row split count for this batch, and the balanced
+ * schedule); with PKV_F_BALANCED it
  * depends on the shape and the current device's compute-unit count, not on
  * the batch or the context lengths.  0 when no workspace is needed or for
  * invalid shapes.  Host function.
@@ -90,8 +91,9 @@ size_t paged_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t n
 
 /*
  * paged_decode_num_splits - the per-row split count paged_decode_attn
- * chooses for num_splits == 0 (without PKV_F_BALANCED) on the current device.
- * Host function.
+ * chooses for num_splits == 0 (without PKV_F_BALANCED) on the current device
+ * when max_kv_len is at most 2048 (above it the automatic choice is the
+ * balanced schedule).  Host function.
  */
 int32_t paged_decode_num_splits(int32_t batch, int32_t num_kv_heads, int32_t max_kv_len);
 
@@ -129,7 +131,10 @@ int32_t paged_decode_balanced_parts(int32_t batch, int32_t num_kv_heads, int32_t
  *                loose bound costs speed, never correctness
  *   num_splits   split-K (flash-decoding; the pages leave the decode kernel's
  *                work split open, so the schedules are the library's own):
- *                0 = automatic per-row split count (paged_decode_num_splits),
+ *                0 = automatic: when the key bound (max_kv_len, else
+ *                    max_blocks*page_size) is at most 2048, the per-row
+ *                    schedule with paged_decode_num_splits splits; above it
+ *                    the balanced schedule below (long or skewed contexts),
  *                1 = one workgroup per (row, KV head), single pass,
  *                2..PKV_MAX_SPLITS = each row's keys in that many equal parts,
  *                    merged by log-sum-exp in a second kernel.

@@ -74,6 +74,10 @@ int device_cus() {
 }
 
 constexpr int kMinSplitKeys = 256;
+// Above this key bound the automatic choice uses the balanced schedule
+// (measured: per-row wins up to 2048 keys, balanced from 2-4k keys on, and by
+// 2-7x when one long row sits among short ones).
+constexpr int32_t kAutoBalancedKeys = 2048;
 
 // Per-row schedule, automatic split count.  One workgroup per (row, KV head)
 // already fills the chip when there are at least as many units as compute
@@ -157,17 +161,18 @@ size_t paged_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t n
   if (num_splits < 0 || batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       num_q_heads % num_kv_heads != 0)
     return 0;
-  if (flags & PKV_F_BALANCED) {
-    const size_t parts = (size_t)num_kv_heads * balanced_max_parts(num_kv_heads, device_cus()) * 2;
-    const size_t rows = parts * (size_t)(num_q_heads / num_kv_heads);
-    return align256(rows * (size_t)head_dim * sizeof(float)) + align256(rows * sizeof(float)) +
-           parts / 2 * 4 * sizeof(int32_t);
-  }
+  const size_t parts = (size_t)num_kv_heads * balanced_max_parts(num_kv_heads, device_cus()) * 2;
+  const size_t brows = parts * (size_t)(num_q_heads / num_kv_heads);
+  const size_t balanced_bytes = align256(brows * (size_t)head_dim * sizeof(float)) +
+                                align256(brows * sizeof(float)) + parts / 2 * 4 * sizeof(int32_t);
+  if (flags & PKV_F_BALANCED) return balanced_bytes;
   // automatic: the largest count auto_splits can pick for this batch, whatever the lengths
   const int32_t S = num_splits ? num_splits : auto_splits(batch, num_kv_heads, INT32_MAX, device_cus());
-  if (S <= 1) return 0;
   const size_t rows = (size_t)S * (size_t)batch * (size_t)num_q_heads;
-  return align256(rows * (size_t)head_dim * sizeof(float)) + rows * sizeof(float);
+  const size_t per_row_bytes =
+      S <= 1 ? 0 : align256(rows * (size_t)head_dim * sizeof(float)) + rows * sizeof(float);
+  // the automatic choice may also pick the balanced schedule (long contexts)
+  return num_splits ? per_row_bytes : std::max(per_row_bytes, balanced_bytes);
 }
 
 int32_t paged_decode_num_splits(int32_t batch, int32_t num_kv_heads, int32_t max_kv_len) {
@@ -215,10 +220,13 @@ static int decode_common(const char *who, const void *q, const void *k_new, cons
 
   const int32_t cap = max_blocks * page_size;
   const int32_t kv_bound = (max_kv_len <= 0 || max_kv_len > cap) ? cap : max_kv_len;
-  const bool balanced = (flags & PKV_F_BALANCED) != 0;
-  if (balanced && num_splits != 0)
+  if ((flags & PKV_F_BALANCED) && num_splits != 0)
     return fail(PKV_E_SPLITS, "PKV_F_BALANCED chooses its own split points: num_splits must be 0 (got %d)",
                 num_splits);
+  // The automatic choice (num_splits 0, no schedule flag) takes the balanced
+  // schedule for long contexts, where one long row would otherwise hold a
+  // few workgroups busy long after the rest of the batch is done.
+  const bool balanced = (flags & PKV_F_BALANCED) != 0 || (num_splits == 0 && kv_bound > kAutoBalancedKeys);
   int32_t S;
   if (balanced) {
     S = balanced_parts(batch, num_kv_heads, kv_bound, device_cus());

@@ -85,6 +85,7 @@ def _decode(lib, **kw):
     (dict(splits=2), -4, "workspace"),
     (dict(splits=2, flags=4), -5, "num_splits"),
     (dict(splits=0, flags=4), -4, "workspace"),
+    (dict(splits=0, max_kv_len=4096, max_blocks=300), -4, "balanced"),   # automatic, long context
     (dict(splits=2, ws=FAKE, ws_bytes=100), -4, "workspace"),
     (dict(splits=2, ws=FAKE + 4, ws_bytes=1 << 20), -3, "workspace"),
 ])
@@ -160,11 +161,6 @@ def test_workspace_size(lib):
     assert ws(2, 4, 2, 128, 3, 0) == o_bytes + rows * 4
     assert ws(0, 4, 2, 128, 3, 0) == 0
     assert ws(2, 5, 2, 128, 3, 0) == 0                 # H_q not a multiple of H_kv
-    # automatic: sized for the largest split count the heuristic can pick
-    s_max = lib.paged_decode_num_splits(2, 2, 1 << 30)
-    rows = s_max * 2 * 4
-    assert ws(2, 4, 2, 128, 0, 0) == (rows * 128 * 4 + 255) // 256 * 256 + rows * 4
-    assert ws(512, 32, 8, 128, 0, 0) == 0              # enough units: single pass
     # balanced: partials for 2 slots per (KV head, workgroup), independent of the batch
     w8 = lib.paged_decode_balanced_parts(100000, 8, 1 << 20)      # the cap: 2*CUs/H_kv
     assert w8 >= 1
@@ -172,6 +168,13 @@ def test_workspace_size(lib):
     assert b == ws(7, 32, 8, 128, 0, 4) > 0
     rows = 8 * w8 * 2 * 4
     assert b == (rows * 128 * 4 + 255) // 256 * 256 + (rows * 4 + 255) // 256 * 256 + 8 * w8 * 16
+    # automatic: covers the largest per-row split count the heuristic can pick and the
+    # balanced schedule, which it takes for long contexts
+    s_max = lib.paged_decode_num_splits(2, 2, 1 << 30)
+    rows = s_max * 2 * 4
+    per_row = (rows * 128 * 4 + 255) // 256 * 256 + rows * 4
+    assert ws(2, 4, 2, 128, 0, 0) == max(per_row, ws(2, 4, 2, 128, 0, 4))
+    assert ws(512, 32, 8, 128, 0, 0) == ws(512, 32, 8, 128, 0, 4)  # single pass, or balanced
 
 
 def test_auto_splits(lib):
