@@ -163,9 +163,10 @@ def paged_decode_attn(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tenso
                       stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Decode attention; returns (out bf16 [B, H_q, D], lse fp32 [B, H_q]).
 
-    num_splits = 0 picks the per-row split count automatically, 1 is a single
-    pass, >1 per-row splits; flags |= PKV_F_BALANCED (with num_splits = 0)
-    selects the balanced schedule.  The workspace (uint8 tensor) is allocated
+    num_splits = 0 chooses automatically (per-row splits up to a key bound of
+    2048, the balanced schedule above it), 1 is a single pass, >1 per-row
+    splits; flags |= PKV_F_BALANCED (with num_splits = 0) forces the balanced
+    schedule.  The workspace (uint8 tensor) is allocated
     here when not given and the schedule needs one.
     """
     L = load_library()
