@@ -84,8 +84,15 @@ __device__ __forceinline__ uint32_t block_row(const RowCtx &c, int key0) {
 
 // K rows of a 32-key tile as QK A-operands.  kbase is the KV head's plane;
 // offsets are 32-bit (a head plane is below 4 GiB).  K and V are streamed
-// once per call, so their loads are non-temporal.
-template <int D>
+// once per call; with kNT the loads are non-temporal, which pays when the
+// call keeps the whole chip streaming and costs latency when it does not.
+template <bool kNT>
+__device__ __forceinline__ u32x4 kv_load(const char *p) {
+  if constexpr (kNT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  return *reinterpret_cast<const u32x4 *>(p);
+}
+
+template <int D, bool kNT>
 __device__ __forceinline__ void load_k(u32x4 (&k)[2][D / 32], const RowCtx &c, const char *kbase,
                                        int kt, int lane) {
   const int hl = lane & 15, lg = lane >> 4;
@@ -94,11 +101,11 @@ __device__ __forceinline__ void load_k(u32x4 (&k)[2][D / 32], const RowCtx &c, c
     const uint32_t off = (block_row(c, kt + 16 * b) + hl) * (2u * D) + 16u * lg;
 #pragma unroll
     for (int ch = 0; ch < D / 32; ++ch)
-      k[b][ch] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kbase + off + 64u * ch));
+      k[b][ch] = kv_load<kNT>(kbase + off + 64u * ch);
   }
 }
 
-template <int D>
+template <int D, bool kNT>
 __device__ __forceinline__ void load_v(u32x4 (&v)[D / 16], const RowCtx &c, const char *vbase,
                                        int kt, int lane) {
   using Gm = DecGeom<D>;
@@ -109,8 +116,7 @@ __device__ __forceinline__ void load_v(u32x4 (&v)[D / 16], const RowCtx &c, cons
   for (int i = 0; i < Gm::kVLoads; ++i) {
     const int first = i * Gm::kKeysPerLoad;                 // first key of this load in the tile
     const uint32_t rb = (first < 16) ? row0 : row1;         // a load never straddles blocks
-    v[i] = __builtin_nontemporal_load(
-        reinterpret_cast<const u32x4 *>(vbase + (rb + (first & 15)) * (2u * D) + lane_off));
+    v[i] = kv_load<kNT>(vbase + (rb + (first & 15)) * (2u * D) + lane_off);
   }
 }
 
@@ -240,7 +246,7 @@ __device__ void write_empty(const PieceOut &dst, int G, int D) {
 // n-1 is the caller's new token: it is attended from k_new/v_new rather than
 // the pool, and written into its page.  Ends with a workgroup barrier, so the
 // caller may start another piece right away.
-template <int D, bool kFused, bool kEarlyNew>
+template <int D, bool kFused, bool kEarlyNew, bool kNT>
 __device__ void decode_piece(const DecodeArgs &a, char *smem, int r, int g, int s, int lo, int hi,
                              bool with_new, const PieceOut &dst, int lane, int wave) {
   if constexpr (!kFused) with_new = false;
@@ -363,21 +369,21 @@ __device__ void decode_piece(const DecodeArgs &a, char *smem, int r, int g, int 
     c.hi = seg_hi;
     const int ntiles = (seg_hi - seg_lo + kTileKeys - 1) / kTileKeys;
     int t = wave;
-    load_v<D>(vr, c, vbase, seg_lo + t * kTileKeys, lane);
-    load_k<D>(ka, c, kbase, seg_lo + t * kTileKeys, lane);
+    load_v<D, kNT>(vr, c, vbase, seg_lo + t * kTileKeys, lane);
+    load_k<D, kNT>(ka, c, kbase, seg_lo + t * kTileKeys, lane);
     while (t < ntiles) {
       store_v<D>(vr, vlds, seg_lo + t * kTileKeys, seg_hi, lane);
       int tn = t + kDecWaves;
-      load_v<D>(vr, c, vbase, seg_lo + tn * kTileKeys, lane);
-      load_k<D>(kb, c, kbase, seg_lo + tn * kTileKeys, lane);
+      load_v<D, kNT>(vr, c, vbase, seg_lo + tn * kTileKeys, lane);
+      load_k<D, kNT>(kb, c, kbase, seg_lo + tn * kTileKeys, lane);
       compute_tile<D>(ka, seg_lo + t * kTileKeys, seg_hi, vlds, qop, m_run, l_run, o,
                       a.scale_log2, lane);
       t = tn;
       if (t >= ntiles) break;
       store_v<D>(vr, vlds, seg_lo + t * kTileKeys, seg_hi, lane);
       tn = t + kDecWaves;
-      load_v<D>(vr, c, vbase, seg_lo + tn * kTileKeys, lane);
-      load_k<D>(ka, c, kbase, seg_lo + tn * kTileKeys, lane);
+      load_v<D, kNT>(vr, c, vbase, seg_lo + tn * kTileKeys, lane);
+      load_k<D, kNT>(ka, c, kbase, seg_lo + tn * kTileKeys, lane);
       compute_tile<D>(kb, seg_lo + t * kTileKeys, seg_hi, vlds, qop, m_run, l_run, o,
                       a.scale_log2, lane);
       t = tn;
@@ -473,7 +479,7 @@ __device__ __forceinline__ int row_keys(const DecodeArgs &a, int r, int &slot, b
 // Per-row schedule: blockIdx.x enumerates (split, KV head, row), split
 // fastest; split sp of a row covers an equal share of its keys in whole
 // 32-key tiles.  With one split the result is final, else a partial.
-template <int D, bool kFused>
+template <int D, bool kFused, bool kNT>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_rows_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[DecGeom<D>::kSmemBytes];
@@ -501,7 +507,7 @@ void decode_rows_kernel(DecodeArgs a) {
     return;
   }
   const bool with_new = has_new && hi == n;
-  decode_piece<D, kFused, true>(a, smem, r, g, s, lo, hi, with_new, dst, lane, wave);
+  decode_piece<D, kFused, true, kNT>(a, smem, r, g, s, lo, hi, with_new, dst, lane, wave);
 }
 
 __device__ __forceinline__ int64_t readlane64(int64_t v, int l) {
@@ -623,7 +629,7 @@ void decode_balanced_kernel(DecodeArgs a) {
             desc_last = (int)((ej * We + TT - 1) / TT) - 1;  // range holding tile ej-1
           }
         }
-        decode_piece<D, kFused, false>(a, smem, rr, g, sj, lo, hi, hnj && hi == nj, dst, lane, wave);
+        decode_piece<D, kFused, false, true>(a, smem, rr, g, sj, lo, hi, hnj && hi == nj, dst, lane, wave);
       }
     }
   }
@@ -744,10 +750,14 @@ __global__ __launch_bounds__(256) void merge_balanced_kernel(DecodeArgs a) {
 
 template <int D, bool kFused>
 static void launch_main(const DecodeArgs &a, dim3 grid, hipStream_t stream) {
+  // The balanced schedule serves long contexts and always streams; the
+  // per-row schedule streams non-temporally when its units fill the chip.
   if (a.balanced)
     hipLaunchKernelGGL((decode_balanced_kernel<D, kFused>), grid, dim3(kDecThreads), 0, stream, a);
+  else if (a.stream_nt)
+    hipLaunchKernelGGL((decode_rows_kernel<D, kFused, true>), grid, dim3(kDecThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_rows_kernel<D, kFused>), grid, dim3(kDecThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_rows_kernel<D, kFused, false>), grid, dim3(kDecThreads), 0, stream, a);
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {

@@ -28,6 +28,7 @@ struct DecodeArgs {
   int32_t balanced;                // 1: balanced schedule, 0: per-row splits
   int32_t num_splits;              // per-row: splits per row; balanced: workgroups per KV head (W)
   int32_t contig_mode;             // 0 detect per row, 1 assume contiguous, 2 never
+  int32_t stream_nt;               // per-row schedule: non-temporal K/V loads
   // Partials.  Per-row: [S][B][H_q][D] and [S][B][H_q].  Balanced: [H_kv][W][2][G][D],
   // [H_kv][W][2][G] and one descriptor per (KV head, workgroup) in desc.
   float *o_part, *lse_part;
