@@ -24,7 +24,10 @@
 //    16 bytes against bank conflicts); the next stage's global loads are in
 //    flight while the current one is used.
 //  * Online softmax in base 2 in fp32; causal masking only on stages that
-//    reach the diagonal.
+//    reach the diagonal.  The weights are computed against the running
+//    reference max straight away; the column max is reduced across lanes
+//    only on the rare step that moves the reference, which then recomputes
+//    them, so the common step has no cross-lane step before its exponentials.
 #include <math.h>
 
 #include "pkv_device.h"
@@ -369,16 +372,24 @@ void prefill_kernel(PrefillArgs a) {
             if (off > lim) x[i] = -INFINITY;
           }
         }
-        float mt = x[0];
+        // Speculative weights against the current reference point m_run; a
+        // lane-local max tests whether it must move (some lane's scores
+        // exceed it by more than kLazy, in log2 units).  The test and the
+        // new reference are those of the column max (max commutes with the
+        // positive scale), so only the rare step that moves it recomputes.
+        float lm = x[0];
 #pragma unroll
-        for (int i = 1; i < 8; ++i) mt = fmaxf(mt, x[i]);
-        mt = max_xor16(mt);
-        mt = max_xor32(mt);
-        mt *= a.scale_log2;
-        // Lazy rescaling: the reference point m_run only moves when some
-        // lane's tile max exceeds it by more than kLazy (log2 units); until
-        // then p <= 2^kLazy and no accumulator needs rescaling.
-        if (__any(mt > m_run[qb] + kLazy)) {
+        for (int i = 1; i < 8; ++i) lm = fmaxf(lm, x[i]);
+        float p[8], ps = 0.f;
+        {
+          const float m_use = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(x[i], a.scale_log2, -m_use));
+        }
+        if (__any(lm * a.scale_log2 > m_run[qb] + kLazy)) {
+          float mt = max_xor16(lm);
+          mt = max_xor32(mt);
+          mt *= a.scale_log2;
           const float m_new = fmaxf(m_run[qb], mt);
           if (__any(m_run[qb] != -INFINITY)) {  // otherwise o and l are still zero
             const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run[qb] - m_new);
@@ -387,14 +398,12 @@ void prefill_kernel(PrefillArgs a) {
             for (int t = 0; t < D / 16; ++t) o[qb][t] *= alpha;
           }
           m_run[qb] = m_new;
-        }
-        const float m_use = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
-        float p[8], ps = 0.f;
+          const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          p[i] = fast_exp2(fmaf(x[i], a.scale_log2, -m_use));
-          ps += p[i];
+          for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(x[i], a.scale_log2, -m_use));
         }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ps += p[i];
         l_run[qb] += ps;
         const u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                           pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
