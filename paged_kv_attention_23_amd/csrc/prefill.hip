@@ -342,6 +342,7 @@ void prefill_kernel(PrefillArgs a) {
     auto softmax_pv = [&](int h2, const f32x4 (&sc)[2][kQB]) {
       const int key0 = s * kPfBN + 32 * h2;  // position of the half's first key
       const bool diag = key0 + 31 >= q_first;  // some key may lie past some query row
+      const bool first = key0 == 0;  // the tile's first step: m_run is still -inf, no speculation
       // V^T operands from transposing LDS reads: lane (hl, lg) of step t
       // gets head_dim d = 32*(t/2) + 8*(hl/4) + 4*(t%2) + hl%4 at keys
       // kappa(lg, 0..3) and kappa(lg, 4..7), the key order of P^T.  All eight are read first, so
@@ -381,12 +382,12 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int i = 1; i < 8; ++i) lm = fmaxf(lm, x[i]);
         float p[8], ps = 0.f;
-        {
+        if (!first) {
           const float m_use = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
 #pragma unroll
           for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(x[i], a.scale_log2, -m_use));
         }
-        if (__any(lm * a.scale_log2 > m_run[qb] + kLazy)) {
+        if (first || __any(lm * a.scale_log2 > m_run[qb] + kLazy)) {
           float mt = max_xor16(lm);
           mt = max_xor32(mt);
           mt *= a.scale_log2;
