@@ -13,7 +13,9 @@
 //    16 contiguous bytes), Q held in B-operand registers for the whole unit
 //    (heads past G are zero columns).
 //  * Online softmax in base 2 in fp32 registers: each lane owns one head and
-//    eight keys of the tile; the tile max needs two cross-row shuffles.
+//    eight keys of the tile.  Weights are taken against a lazily moved
+//    reference max; only a tile that exceeds it by the lazy threshold pays
+//    for the two cross-row shuffles of the tile max and the rescale.
 //  * O^T[d][head] += V^T P^T on the matrix core.  The score layout already is
 //    the B operand P^T (key order permuted consistently); V^T comes from a
 //    per-wave LDS tile through gfx950's transposing LDS reads, its key rows
@@ -33,6 +35,7 @@ namespace pkv {
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = kDecWaves * kWave;
 constexpr int kTileKeys = 32;
+constexpr float kDecLazy = 8.f;  // lazy-rescale threshold, log2 units
 
 template <int D>
 struct DecGeom {
@@ -168,25 +171,36 @@ __device__ __forceinline__ void compute_tile(const u32x4 (&k)[2][D / 32], int kt
       if (key >= hi) x[i] = -INFINITY;
     }
   }
-  float mt = x[0];
+  // Weights against the running reference m_run, computed straight away;
+  // the reference moves (cross-lane max, rescale, recompute) only when some
+  // lane's scores exceed it by more than kDecLazy (log2 units), so the
+  // common tile has no cross-lane step and no accumulator rescale.
+  float lm = x[0];
 #pragma unroll
-  for (int i = 1; i < 8; ++i) mt = fmaxf(mt, x[i]);
-  mt = max_xor16(mt);
-  mt = max_xor32(mt);
-  const float m_new = fmaxf(m_run, mt);
-  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-  const float alpha = fast_exp2(m_run - m_use);
+  for (int i = 1; i < 8; ++i) lm = fmaxf(lm, x[i]);
   float p[8];
+  {
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = fast_exp2(x[i] - m_use);
+  }
+  if (__any(lm > m_run + kDecLazy)) {
+    float mt = max_xor16(lm);
+    mt = max_xor32(mt);
+    const float m_new = fmaxf(m_run, mt);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);  // 0 while m_run = -inf
+    l_run *= alpha;
+#pragma unroll
+    for (int t = 0; t < Gm::kDBlocks; ++t) o[t] *= alpha;
+    m_run = m_new;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = fast_exp2(x[i] - m_use);
+  }
   float psum = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    p[i] = fast_exp2(x[i] - m_use);
-    psum += p[i];
-  }
-  l_run = l_run * alpha + psum;
-  m_run = m_new;
-#pragma unroll
-  for (int t = 0; t < Gm::kDBlocks; ++t) o[t] *= alpha;
+  for (int i = 0; i < 8; ++i) psum += p[i];
+  l_run += psum;
 
   // 3) P^T is already in B-operand form: element e of k-group lg is key
   //    kappa(lg, e) = e < 4 ? 4*lg + e : 16 + 4*lg + (e - 4).
