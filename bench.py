@@ -316,6 +316,10 @@ def main():
     pa_total = timed(prefill["attn"], K) if prefill else 0.0
     palt_total = timed(prefill["alt"], K) if prefill else 0.0
     ch_total = timed(chunked["step"], K) if chunked else 0.0
+    # warm, for context: every call reads the same cache (input set), which
+    # then sits in the 256 MiB Infinity Cache; not an HBM figure
+    dw_total = timed(lambda i: decode_only(0), K)
+    pw_total = timed(lambda i: prefill["attn"](0), K) if prefill else 0.0
 
     dec_ms, dk_ms = dec_total / K, dk_total / K
     value = kv_bytes / (dec_ms * 1e-3) / 1e9
@@ -364,6 +368,9 @@ def main():
             "traffic": measured_traffic("decode", "decode.hip"),
             "avg_call_us": round(dk_ms * 1e3, 3),
             "algorithmic_bytes_per_call": int(kv_bytes),
+            "warm_call_us": round(dw_total / K * 1e3, 3),
+            "warm_gbs": round(kv_bytes / (dw_total / K * 1e-3) / 1e9, 2),
+            "warm": "the same KV cache every call (Infinity-Cache resident), context only",
         },
         "wall_s_timed_region": round(wall, 3),
     }
@@ -396,6 +403,9 @@ def main():
                 "compulsory_bytes": int(p_bytes),
                 "hbm_achieved_gbs": round(p_bytes / (pa_ms * 1e-3) / 1e9, 2),
                 "hbm_frac": round(p_bytes / (pa_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "warm_attn_us": round(pw_total / K * 1e3, 3),
+                "warm_tflops": round(flops / (pw_total / K * 1e-3) / 1e12, 2),
+                "warm": "the same input set every call (Infinity-Cache resident), context only",
             },
             "cache": f"cold: {prefill['layers']} input sets read round-robin",
         }
