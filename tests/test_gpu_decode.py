@@ -311,6 +311,22 @@ def test_decode_needles():
         assert np.abs(o[-1] - 5.0).min() > 1.0   # key n never admitted
 
 
+def test_decode_growing_scores():
+    """Key magnitudes vary from page to page by up to 26x, so each wave's running
+    reference max moves many times along its tiles (rescale and recompute path)."""
+    _print_case("decode growing scores")
+    c = _small_case(61, 8, 2, 128, 16, [1500, 700, 33, 1024], "shuffled")
+    rows = np.arange(c.k_pool.shape[1])
+    f = (1.0 + (rows // c.page_size % 97) / 3.7).astype(np.float32)
+    c.k_pool[:] = f32_to_bf16_bits(bf16_bits_to_f32(c.k_pool) * f[None, :, None])
+    out_ref, lse_ref = oracle.decode_case(c)
+    d = _Dev(c)
+    for S in (1, 4):
+        out, lse = d.decode(num_splits=S)
+        torch.cuda.synchronize()
+        check_close(out, lse, out_ref, lse_ref, f"growing scores/S{S}")
+
+
 def test_decode_shape_sequence():
     """Small, then large, then medium batches in one process (no shape specialisation)."""
     _print_case("decode shape sequence")

@@ -1,13 +1,14 @@
 """GPU parity of packed_prefill_attn against the float64 oracle."""
 from __future__ import annotations
 
+import dataclasses
 import functools
 
 import numpy as np
 import pytest
 
 import oracle
-from workloads import BF16_NAN, make_case, make_prefill_case
+from workloads import BF16_NAN, bf16_bits_to_f32, f32_to_bf16_bits, make_case, make_prefill_case
 
 pytestmark = pytest.mark.gpu
 
@@ -61,6 +62,23 @@ def test_prefill_edge_shapes(spec):
     out_ref, lse_ref = oracle.prefill_case(pc)
     out, lse = _run(pc)
     check_close(out, lse, out_ref, lse_ref, f"prefill seed{seed}")
+
+
+def test_prefill_growing_scores():
+    """Key magnitudes grow along each document, with spikes late in it, so the running
+    reference max of a query row moves again and again inside its tile: the path that
+    rescales the accumulators and recomputes a step's weights, against the oracle."""
+    print("prefill growing scores", flush=True)
+    pc = make_prefill_case(name="grow", seed=59, doc_lens=[700, 129, 300, 33], H_q=32, H_kv=8,
+                           D=128, page_size=128, num_pages=64, max_blocks=8)
+    pos = np.concatenate([np.arange(n) for n in pc.doc_lens()])
+    f = (1.0 + pos / 48.0) * np.where(pos % 257 == 200, 4.0, 1.0)
+    k = f32_to_bf16_bits(bf16_bits_to_f32(pc.k) * f.astype(np.float32)[:, None, None])
+    pc = dataclasses.replace(pc, k=k)
+    out_ref, lse_ref = oracle.prefill_case(pc)
+    assert np.ptp(lse_ref) > 50.0  # the scores really span a wide range
+    out, lse = _run(pc)
+    check_close(out, lse, out_ref, lse_ref, "prefill growing scores")
 
 
 def test_prefill_document_order_and_determinism():
