@@ -74,12 +74,24 @@ __device__ __forceinline__ int ceil_div_qt(int x, int QT, int qt_shift) {
   return qt_shift >= 0 ? (x + QT - 1) >> qt_shift : (x + QT - 1) / QT;
 }
 
-__device__ bool find_tile(const int32_t *cu, int num_docs, int QT, int qt_shift, int tile, int lane,
-                          PfTile &out) {
+// Document bounds are clamped to [0, L] (and the end to no less than the
+// start), so out-of-contract cu_seqlens can never place a row outside the
+// packed arrays; for valid bounds the clamps change nothing.
+__device__ __forceinline__ int doc_lo(const int32_t *cu, int d, int L) { return min(max(cu[d], 0), L); }
+__device__ __forceinline__ int doc_hi(const int32_t *cu, int d, int lo, int L) {
+  return min(max(cu[d + 1], lo), L);
+}
+
+__device__ bool find_tile(const int32_t *cu, int num_docs, int L, int QT, int qt_shift, int tile,
+                          int lane, PfTile &out) {
   int base = 0;  // tiles of the documents before this chunk
   for (int d0 = 0; d0 < num_docs; d0 += kWave) {
     const int d = d0 + lane;
-    const int t = (d < num_docs) ? ceil_div_qt(cu[d + 1] - cu[d], QT, qt_shift) : 0;
+    int t = 0;
+    if (d < num_docs) {
+      const int lo = doc_lo(cu, d, L);
+      t = ceil_div_qt(doc_hi(cu, d, lo, L) - lo, QT, qt_shift);
+    }
     int incl = t;  // inclusive prefix sum of tile counts over the chunk
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
@@ -93,10 +105,10 @@ __device__ bool find_tile(const int32_t *cu, int num_docs, int QT, int qt_shift,
       const int end = base + __shfl(incl, j, kWave);
       const int qt = end - 1 - tile;  // query tile inside the document, last first
       out.doc = dd;
-      out.doc_start = cu[dd];
-      out.doc_end = cu[dd + 1];
-      out.q_lo = cu[dd] + qt * QT;
-      out.q_hi = min(cu[dd + 1], out.q_lo + QT);
+      out.doc_start = doc_lo(cu, dd, L);
+      out.doc_end = doc_hi(cu, dd, out.doc_start, L);
+      out.q_lo = out.doc_start + qt * QT;
+      out.q_hi = min(out.doc_end, out.q_lo + QT);
       return true;
     }
     base += __shfl(incl, kWave - 1, kWave);
@@ -120,7 +132,7 @@ void prefill_kernel(PrefillArgs a) {
   const int qt_shift = (QT & (QT - 1)) == 0 ? __builtin_ctz(QT) : -1;
 
   PfTile tl;
-  if (!find_tile(a.cu_seqlens, a.num_docs, QT, qt_shift, tile, lane, tl)) return;  // uniform
+  if (!find_tile(a.cu_seqlens, a.num_docs, a.L, QT, qt_shift, tile, lane, tl)) return;  // uniform
   tl.doc = __builtin_amdgcn_readfirstlane(tl.doc);  // uniform values: keep them in SGPRs
   tl.doc_start = __builtin_amdgcn_readfirstlane(tl.doc_start);
   tl.doc_end = __builtin_amdgcn_readfirstlane(tl.doc_end);
