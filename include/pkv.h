@@ -298,6 +298,74 @@ int paged_prefill_attn(const void *q, const void *k, const void *v, const int32_
                        int32_t num_slots, int32_t max_blocks, void *out, float *lse,
                        void *stream);
 
+/* Violation codes written by pkv_validate_decode / pkv_validate_prefill. */
+#define PKV_V_SLOT 1     /* batch slot outside [0, num_slots) */
+#define PKV_V_LEN 2      /* negative kv_len or prefix length */
+#define PKV_V_CAPACITY 3 /* a live row's keys exceed max_blocks*page_size */
+#define PKV_V_PAGE 4     /* a page id of a live block outside [1, num_pages) */
+#define PKV_V_BOUNDS 5   /* cu_seqlens not 0 at the start, decreasing, or not total_len at the end */
+
+/*
+ * pkv_validate_decode - debug check of the device-side inputs of
+ * paged_decode_attn and paged_decode_attn_append.
+ *
+ * The attention kernels take these values on trust and clamp them so that no
+ * access leaves the buffers (results for out-of-contract values are
+ * unspecified); this call reports them instead.  It is meant for debug
+ * builds and tests, not the serving loop.  Row r is checked for:
+ *   batch_idx[r] in [0, num_slots)                               (PKV_V_SLOT)
+ *   kv_len[r] >= 0                                               (PKV_V_LEN)
+ * and, for a live row (batch_idx[r] > 0, kv_len[r] > 0), the conditions of
+ * the decode step of the qwen3_flex_inference.py page (its valid keys are
+ * positions 0 .. kv_len-1, mapped through the page table):
+ *   kv_len[r] <= max_blocks * page_size                          (PKV_V_CAPACITY)
+ *   page_table[batch_idx[r]][j] in [1, num_pages) for every block j holding
+ *   a valid key (page 0 is the reserved padding page)            (PKV_V_PAGE)
+ *
+ *   page_table          int32 [num_slots][max_blocks], device
+ *   batch_idx, kv_len   int32 [batch], device
+ *   report              int32 [4], device, written (nothing needs clearing):
+ *                       { number of violating rows, first violating row or -1,
+ *                         its PKV_V_* code or 0, the block for PKV_V_PAGE or -1 }
+ *
+ * One small kernel is enqueued on `stream`; read `report` after it.  Shapes
+ * follow paged_decode_attn (page_size a power of two >= 16); batch == 0
+ * writes an empty report.
+ */
+int pkv_validate_decode(const int32_t *page_table, int32_t num_pages, int32_t page_size,
+                        int32_t num_slots, int32_t max_blocks, const int32_t *batch_idx,
+                        const int32_t *kv_len, int32_t batch, int32_t *report, void *stream);
+
+/*
+ * pkv_validate_prefill - debug check of the device-side inputs of
+ * packed_prefill_attn, packed_prefill_attn_append and paged_prefill_attn.
+ *
+ * Document d (d < num_docs) is checked for:
+ *   cu_seqlens[0] == 0, cu_seqlens[d+1] >= cu_seqlens[d],
+ *   cu_seqlens[num_docs] == total_len                            (PKV_V_BOUNDS)
+ * with doc_slots (NULL: not checked):
+ *   doc_slots[d] in [0, num_slots)                               (PKV_V_SLOT)
+ * with prefix_lens as well (NULL: no cached prefix), for paged_prefill_attn:
+ *   prefix_lens[d] >= 0                                          (PKV_V_LEN)
+ * and for a document in a slot > 0:
+ *   prefix_lens[d] + n_d <= max_blocks * page_size               (PKV_V_CAPACITY)
+ *   the page ids of the blocks holding the cached prefix lie in [1, num_pages)
+ *   (the chunk's own rows are written with paged_kv_append's skip rules)
+ *                                                                (PKV_V_PAGE)
+ *
+ *   cu_seqlens    int32 [num_docs+1], device
+ *   doc_slots     int32 [num_docs], device, or NULL
+ *   prefix_lens   int32 [num_docs], device, or NULL (needs doc_slots)
+ *   page_table    int32 [num_slots][max_blocks], device; needed with doc_slots
+ *   report        int32 [4] as in pkv_validate_decode, documents in place of rows
+ *
+ * Without doc_slots the page arguments are ignored.
+ */
+int pkv_validate_prefill(const int32_t *cu_seqlens, int32_t num_docs, int32_t total_len,
+                         const int32_t *doc_slots, const int32_t *prefix_lens,
+                         const int32_t *page_table, int32_t num_pages, int32_t page_size,
+                         int32_t num_slots, int32_t max_blocks, int32_t *report, void *stream);
+
 /* Text for the most recent non-zero status returned on this thread. */
 const char *pkv_last_error(void);
 

@@ -16,6 +16,8 @@ libpkv.so (include/pkv.h):
                        into their pages, in one launch
   paged_prefill_attn   chunked prefill: chunks attend to their sequence's
                        cached prefix (pages) and to themselves causally
+  validate_decode, validate_prefill
+                       debug checks of the device-side index inputs
 
 This package is the thin Python binding: it marshals torch tensors into the
 C calls and nothing else.
@@ -37,4 +39,6 @@ from ._binding import (  # noqa: F401
     paged_decode_workspace_size,
     paged_kv_append,
     paged_prefill_attn,
+    validate_decode,
+    validate_prefill,
 )

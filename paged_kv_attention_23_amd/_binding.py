@@ -82,6 +82,10 @@ def load_library(path: str = LIB_PATH):
                                      ctypes.c_float, _P, _P, _I32, _I32, _P, _I32, _I32, _P, _P,
                                      _P]
     L.paged_prefill_attn.restype = ctypes.c_int
+    L.pkv_validate_decode.argtypes = [_P, _I32, _I32, _I32, _I32, _P, _P, _I32, _P, _P]
+    L.pkv_validate_decode.restype = ctypes.c_int
+    L.pkv_validate_prefill.argtypes = [_P, _I32, _I32, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P]
+    L.pkv_validate_prefill.restype = ctypes.c_int
     L.pkv_last_error.argtypes = []
     L.pkv_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -334,3 +338,49 @@ def paged_prefill_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seq
         _stream(stream))
     _check(rc, "paged_prefill_attn")
     return out, lse
+
+
+def validate_decode(page_table: torch.Tensor, batch_idx: torch.Tensor, kv_len: torch.Tensor,
+                    page_size: int, num_pages: int, report: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """Debug check of decode's device-side inputs.  Returns the int32 report [4] on the GPU:
+    (violating rows, first violating row or -1, its PKV_V_* code, block or -1)."""
+    L = load_library()
+    B = batch_idx.shape[0]
+    if kv_len.shape[0] != B:
+        raise ValueError("kv_len and batch_idx differ in length")
+    num_slots, max_blocks = page_table.shape
+    if report is None:
+        report = torch.empty(4, dtype=torch.int32, device=batch_idx.device)
+    rc = L.pkv_validate_decode(_dev(page_table, "page_table", torch.int32, 2), num_pages, page_size,
+                               num_slots, max_blocks, _dev(batch_idx, "batch_idx", torch.int32, 1),
+                               _dev(kv_len, "kv_len", torch.int32, 1), B,
+                               _dev(report, "report", torch.int32, 1), _stream(stream))
+    _check(rc, "pkv_validate_decode")
+    return report
+
+
+def validate_prefill(cu_seqlens: torch.Tensor, total_len: int,
+                     doc_slots: Optional[torch.Tensor] = None,
+                     prefix_lens: Optional[torch.Tensor] = None,
+                     page_table: Optional[torch.Tensor] = None, page_size: int = 16,
+                     num_pages: int = 1, report: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """Debug check of the prefill calls' device-side inputs.  Returns the int32 report [4]
+    on the GPU: (violating documents, first violating document or -1, its PKV_V_* code,
+    block or -1)."""
+    L = load_library()
+    n_docs = cu_seqlens.shape[0] - 1
+    num_slots, max_blocks = page_table.shape if page_table is not None else (1, 1)
+    for t, name in ((doc_slots, "doc_slots"), (prefix_lens, "prefix_lens")):
+        if t is not None and t.shape[0] != n_docs:
+            raise ValueError(f"{name} must have one entry per document")
+    if report is None:
+        report = torch.empty(4, dtype=torch.int32, device=cu_seqlens.device)
+    opt = lambda t, name, nd: _dev(t, name, torch.int32, nd) if t is not None else None  # noqa: E731
+    rc = L.pkv_validate_prefill(_dev(cu_seqlens, "cu_seqlens", torch.int32, 1), n_docs, total_len,
+                                opt(doc_slots, "doc_slots", 1), opt(prefix_lens, "prefix_lens", 1),
+                                opt(page_table, "page_table", 2), num_pages, page_size, num_slots,
+                                max_blocks, _dev(report, "report", torch.int32, 1), _stream(stream))
+    _check(rc, "pkv_validate_prefill")
+    return report

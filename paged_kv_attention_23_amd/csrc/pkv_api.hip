@@ -122,6 +122,78 @@ extern "C" {
 
 const char *pkv_last_error(void) { return g_err; }
 
+// Shape checks of the page arguments shared by the two validation calls.
+static int check_pages(const char *who, int32_t num_pages, int32_t page_size, int32_t num_slots,
+                       int32_t max_blocks) {
+  if (log2_exact(page_size) < 4 || page_size > (1 << 20))
+    return fail(PKV_E_SHAPE, "%s: page_size must be a power of two in [16, 2^20] (got %d)", who,
+                page_size);
+  if (num_pages <= 0 || num_slots <= 0 || max_blocks <= 0)
+    return fail(PKV_E_SHAPE, "%s: num_pages, num_slots and max_blocks must be positive (got %d, %d, %d)",
+                who, num_pages, num_slots, max_blocks);
+  return PKV_OK;
+}
+
+int pkv_validate_decode(const int32_t *page_table, int32_t num_pages, int32_t page_size,
+                        int32_t num_slots, int32_t max_blocks, const int32_t *batch_idx,
+                        const int32_t *kv_len, int32_t batch, int32_t *report, void *stream) {
+  const char *who = "pkv_validate_decode";
+  if (batch < 0) return fail(PKV_E_SHAPE, "%s: batch must be >= 0 (got %d)", who, batch);
+  int rc = check_pages(who, num_pages, page_size, num_slots, max_blocks);
+  if (rc) return rc;
+  if (!report || (batch > 0 && (!page_table || !batch_idx || !kv_len)))
+    return fail(PKV_E_NULL, "%s: a required pointer is NULL", who);
+  if (!aligned4(report) || !aligned4(page_table) || !aligned4(batch_idx) || !aligned4(kv_len))
+    return fail(PKV_E_ALIGN, "%s: int32 arrays must be 4-byte aligned", who);
+  pkv::ValidateArgs a = {};
+  a.page_table = page_table;
+  a.batch_idx = batch_idx;
+  a.kv_len = kv_len;
+  a.batch = batch;
+  a.num_pages = num_pages;
+  a.page_shift = log2_exact(page_size);
+  a.num_slots = num_slots;
+  a.max_blocks = max_blocks;
+  a.report = report;
+  return launch_status(pkv::launch_validate(a, (hipStream_t)stream), who);
+}
+
+int pkv_validate_prefill(const int32_t *cu_seqlens, int32_t num_docs, int32_t total_len,
+                         const int32_t *doc_slots, const int32_t *prefix_lens,
+                         const int32_t *page_table, int32_t num_pages, int32_t page_size,
+                         int32_t num_slots, int32_t max_blocks, int32_t *report, void *stream) {
+  const char *who = "pkv_validate_prefill";
+  if (num_docs < 0 || total_len < 0)
+    return fail(PKV_E_SHAPE, "%s: num_docs and total_len must be >= 0 (got %d, %d)", who, num_docs,
+                total_len);
+  if (!cu_seqlens || !report) return fail(PKV_E_NULL, "%s: a required pointer is NULL", who);
+  if (prefix_lens && !doc_slots)
+    return fail(PKV_E_NULL, "%s: prefix_lens needs doc_slots", who);
+  if (doc_slots) {
+    int rc = check_pages(who, num_pages, page_size, num_slots, max_blocks);
+    if (rc) return rc;
+    if (!page_table) return fail(PKV_E_NULL, "%s: doc_slots needs page_table", who);
+  }
+  if (!aligned4(cu_seqlens) || !aligned4(report) || !aligned4(doc_slots) ||
+      !aligned4(prefix_lens) || !aligned4(page_table))
+    return fail(PKV_E_ALIGN, "%s: int32 arrays must be 4-byte aligned", who);
+  pkv::ValidateArgs a = {};
+  a.cu_seqlens = cu_seqlens;
+  a.doc_slots = doc_slots;
+  a.prefix_lens = prefix_lens;
+  a.page_table = doc_slots ? page_table : nullptr;
+  a.batch = num_docs;
+  a.total_len = total_len;
+  if (doc_slots) {
+    a.num_pages = num_pages;
+    a.page_shift = log2_exact(page_size);
+    a.num_slots = num_slots;
+    a.max_blocks = max_blocks;
+  }
+  a.report = report;
+  return launch_status(pkv::launch_validate(a, (hipStream_t)stream), who);
+}
+
 int paged_kv_append(void *k_pool, void *v_pool, int32_t num_pages, int32_t page_size,
                     int32_t num_kv_heads, int32_t head_dim, const int32_t *page_table,
                     int32_t num_slots, int32_t max_blocks, const int32_t *batch_idx,

@@ -60,7 +60,20 @@ struct PrefillArgs {
   int32_t num_pages, page_shift, num_slots, max_blocks;
 };
 
+// Debug checks (pkv_validate_decode / pkv_validate_prefill).  Decode: rows
+// r < batch with batch_idx/kv_len.  Prefill (cu_seqlens non-NULL): documents
+// d < batch, with doc_slots and prefix_lens optional (NULL).
+struct ValidateArgs {
+  const int32_t *page_table;       // [num_slots][max_blocks], or NULL when no page is checked
+  const int32_t *batch_idx, *kv_len;
+  const int32_t *cu_seqlens, *doc_slots, *prefix_lens;
+  int32_t batch, total_len;
+  int32_t num_pages, page_shift, num_slots, max_blocks;
+  int32_t *report;                 // [4]: count, first index, code, block
+};
+
 hipError_t launch_kv_append(const AppendArgs &a, hipStream_t stream);
+hipError_t launch_validate(const ValidateArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 

@@ -153,6 +153,26 @@ def test_prefill_checks(lib):
     assert "2^24" in B.last_error()
 
 
+def test_validate_checks(lib):
+    """The debug validation calls reject bad shapes and pointers on the host."""
+    f = lib.pkv_validate_decode
+    assert f(FAKE, 8, 16, 3, 4, FAKE, FAKE, -1, FAKE, 0) == -2                  # batch < 0
+    assert f(FAKE, 8, 24, 3, 4, FAKE, FAKE, 2, FAKE, 0) == -2                   # page_size
+    assert f(FAKE, 0, 16, 3, 4, FAKE, FAKE, 2, FAKE, 0) == -2                   # num_pages
+    assert f(FAKE, 8, 16, 3, 4, FAKE, FAKE, 2, 0, 0) == -1                      # report
+    assert f(0, 8, 16, 3, 4, FAKE, FAKE, 2, FAKE, 0) == -1                      # page_table
+    assert f(FAKE, 8, 16, 3, 4, FAKE + 2, FAKE, 2, FAKE, 0) == -3               # alignment
+    g = lib.pkv_validate_prefill
+    assert g(FAKE, -1, 10, 0, 0, 0, 1, 16, 1, 1, FAKE, 0) == -2                 # num_docs < 0
+    assert g(0, 1, 10, 0, 0, 0, 1, 16, 1, 1, FAKE, 0) == -1                     # cu_seqlens
+    assert g(FAKE, 1, 10, 0, FAKE, 0, 1, 16, 1, 1, FAKE, 0) == -1               # prefix w/o slots
+    assert g(FAKE, 1, 10, FAKE, 0, 0, 8, 16, 3, 4, FAKE, 0) == -1               # slots w/o table
+    assert g(FAKE, 1, 10, FAKE, 0, FAKE, 8, 20, 3, 4, FAKE, 0) == -2            # page_size
+    assert g(FAKE + 1, 1, 10, 0, 0, 0, 1, 16, 1, 1, FAKE, 0) == -3              # alignment
+    assert "pkv_validate_prefill" in B.last_error()
+    assert B._C["PKV_V_SLOT"] == 1 and B._C["PKV_V_BOUNDS"] == 5
+
+
 def test_workspace_size(lib):
     ws = lib.paged_decode_workspace_size
     assert ws(4, 32, 8, 128, 1, 0) == 0
