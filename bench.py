@@ -252,8 +252,9 @@ def main():
         if args.flush else None
     flush_sink = torch.empty((), dtype=torch.float32, device=dev)
 
-    def timed(fn, n):
-        """Device time (ms) of n steps fn(0..n-1)."""
+    def timed(fn, n, replays=None):
+        """Device time (ms) of n steps fn(0..n-1).  With a list `replays`, the captured
+        graph is replayed 5 more times and each replay's time (ms) is appended to it."""
         if args.flush:  # each call alone after a 1 GiB read (clean eviction)
             total = 0.0
             for i in range(n):
@@ -292,7 +293,15 @@ def main():
         graph.replay()
         e1.record(stream)
         e1.synchronize()
-        return e0.elapsed_time(e1)
+        total = e0.elapsed_time(e1)
+        if replays is not None:
+            for _ in range(5):
+                e0.record(stream)
+                graph.replay()
+                e1.record(stream)
+                e1.synchronize()
+                replays.append(e0.elapsed_time(e1))
+        return total
 
     # ---------------- warmup
     for i in range(args.warmup):
@@ -311,9 +320,10 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     # the dominant kernels alone (roofline): decode attention, prefill attention
-    dk_total = timed(decode_only, K)
+    dk_reps, pa_reps = [], []
+    dk_total = timed(decode_only, K, dk_reps)
     alt_total = timed(decode_step_fused if args.separate else decode_step_separate, K)
-    pa_total = timed(prefill["attn"], K) if prefill else 0.0
+    pa_total = timed(prefill["attn"], K, pa_reps) if prefill else 0.0
     palt_total = timed(prefill["alt"], K) if prefill else 0.0
     ch_total = timed(chunked["step"], K) if chunked else 0.0
     # warm, for context: every call reads the same cache (input set), which
@@ -368,6 +378,9 @@ def main():
             "traffic": measured_traffic("decode", "decode.hip"),
             "avg_call_us": round(dk_ms * 1e3, 3),
             "algorithmic_bytes_per_call": int(kv_bytes),
+            "replays_us": ({"median": round(float(np.median(dk_reps)) / K * 1e3, 3),
+                            "best": round(min(dk_reps) / K * 1e3, 3), "n": len(dk_reps)}
+                           if dk_reps else None),
             "warm_call_us": round(dw_total / K * 1e3, 3),
             "warm_gbs": round(kv_bytes / (dw_total / K * 1e-3) / 1e9, 2),
             "warm": "the same KV cache every call (Infinity-Cache resident), context only",
@@ -403,6 +416,9 @@ def main():
                 "compulsory_bytes": int(p_bytes),
                 "hbm_achieved_gbs": round(p_bytes / (pa_ms * 1e-3) / 1e9, 2),
                 "hbm_frac": round(p_bytes / (pa_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "replays_us": ({"median": round(float(np.median(pa_reps)) / K * 1e3, 3),
+                                "best": round(min(pa_reps) / K * 1e3, 3), "n": len(pa_reps)}
+                               if pa_reps else None),
                 "warm_attn_us": round(pw_total / K * 1e3, 3),
                 "warm_tflops": round(flops / (pw_total / K * 1e-3) / 1e12, 2),
                 "warm": "the same input set every call (Infinity-Cache resident), context only",
