@@ -51,7 +51,7 @@ __device__ int check_prefill_doc(const ValidateArgs &a, int d, int *blk) {
   if (p < 0) return PKV_V_LEN;
   if (s == 0) return 0;  // padding document
   const int64_t cap = (int64_t)a.max_blocks << a.page_shift;
-  if ((int64_t)p + (hi - lo) > cap) return PKV_V_CAPACITY;
+  if ((int64_t)p + ((int64_t)hi - lo) > cap) return PKV_V_CAPACITY;
   // the cached prefix is read through the page table; the chunk's own rows
   // are written with the append's skip rules, so only prefix blocks count
   const int64_t nblk = ((int64_t)p + (1 << a.page_shift) - 1) >> a.page_shift;
