@@ -327,6 +327,23 @@ def test_decode_growing_scores():
         check_close(out, lse, out_ref, lse_ref, f"growing scores/S{S}")
 
 
+@pytest.mark.parametrize("scale", [1.0, 1e-3])
+def test_decode_scale_extremes(scale):
+    """scale 1 and 1e-3 through every schedule, against the oracle."""
+    _print_case(f"decode scale {scale}")
+    c = make_decode_case(name="scale", seed=62, H_q=32, H_kv=8, D=128, page_size=16,
+                         num_pages=400, num_slots=6, max_blocks=80, row_slots=[1, 2, 0, 3, 4, 5],
+                         row_lens=[1200, 37, 9, 640, 1, 300], layout="shuffled", fill="nan",
+                         scale=scale)
+    out_ref, lse_ref = oracle.decode_case(c)
+    d = _Dev(c)
+    for splits in (1, 3, 0, "balanced"):
+        S, extra = _sched(splits)
+        out, lse = d.decode(num_splits=S, flags=extra)
+        torch.cuda.synchronize()
+        check_close(out, lse, out_ref, lse_ref, f"scale {scale} splits {splits}")
+
+
 def test_decode_shape_sequence():
     """Small, then large, then medium batches in one process (no shape specialisation)."""
     _print_case("decode shape sequence")

@@ -81,6 +81,18 @@ def test_prefill_growing_scores():
     check_close(out, lse, out_ref, lse_ref, "prefill growing scores")
 
 
+@pytest.mark.parametrize("scale", [1.0, 1e-3])
+def test_prefill_scale_extremes(scale):
+    """scale 1 (scores ~11x larger than at 1/sqrt(D): the running max moves often) and
+    scale 1e-3 (near-uniform weights), against the oracle."""
+    print(f"prefill scale {scale}", flush=True)
+    pc = make_prefill_case(name="scale", seed=60, doc_lens=[333, 64, 1, 200], H_q=32, H_kv=8,
+                           D=128, page_size=128, num_pages=64, max_blocks=8, scale=scale)
+    out_ref, lse_ref = oracle.prefill_case(pc)
+    out, lse = _run(pc)
+    check_close(out, lse, out_ref, lse_ref, f"prefill scale {scale}")
+
+
 def test_prefill_document_order_and_determinism():
     """Permuting documents permutes rows bit for bit; repeated calls are bitwise equal."""
     print("prefill permutation", flush=True)
