@@ -93,6 +93,21 @@ def test_prefill_scale_extremes(scale):
     check_close(out, lse, out_ref, lse_ref, f"prefill scale {scale}")
 
 
+def test_prefill_shape_sequence():
+    """Small, then large, then medium packed lengths in one process: nothing is specialised
+    on L (the reference's block-mask specialisation broke the larger L)."""
+    print("prefill shape sequence", flush=True)
+    small = make_prefill_case(name="seq", seed=63, doc_lens=[3, 1, 20], H_q=32, H_kv=8, D=128,
+                              page_size=128, num_pages=8, max_blocks=2)
+    medium = make_prefill_case(name="seq", seed=64, doc_lens=[700, 90, 300], H_q=32, H_kv=8,
+                               D=128, page_size=128, num_pages=32, max_blocks=8)
+    large, (out_l, lse_l) = _cfg5()
+    for pc, ref in ((small, None), (large, (out_l, lse_l)), (medium, None), (small, None)):
+        out_ref, lse_ref = ref if ref is not None else oracle.prefill_case(pc)
+        out, lse = _run(pc)
+        check_close(out, lse, out_ref, lse_ref, f"prefill L={pc.L}")
+
+
 def test_prefill_document_order_and_determinism():
     """Permuting documents permutes rows bit for bit; repeated calls are bitwise equal."""
     print("prefill permutation", flush=True)
