@@ -107,16 +107,31 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _dev(t: torch.Tensor, name: str, dtype, ndim: int) -> int:
+def _dev(t: torch.Tensor, name: str, dtype, ndim: int, shape=None, device=None) -> int:
+    """Data pointer of a contiguous GPU tensor, after checking dtype, rank, and (when
+    given) the exact shape and the device.  The C ABI sees pointers only, so every
+    buffer a kernel writes is checked here against the size the kernel will use."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be on the GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the call runs on {device}")
     if t.dim() != ndim or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous {ndim}-d tensor, got {tuple(t.shape)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     return t.data_ptr()
+
+
+def _workspace(workspace: Optional[torch.Tensor], device) -> Tuple[int, int]:
+    """(pointer, bytes) of an optional uint8 workspace on the call's device."""
+    if workspace is None:
+        return 0, 0
+    ptr = _dev(workspace, "workspace", torch.uint8, 1, device=device)
+    return ptr, workspace.numel()
 
 
 def paged_kv_append(k_pool: torch.Tensor, v_pool: torch.Tensor, page_table: torch.Tensor,
@@ -127,21 +142,18 @@ def paged_kv_append(k_pool: torch.Tensor, v_pool: torch.Tensor, page_table: torc
     H_kv, rows, D = k_pool.shape
     if rows % page_size:
         raise ValueError("pool rows must be a multiple of page_size")
-    if v_pool.shape != k_pool.shape:
-        raise ValueError("k_pool and v_pool differ in shape")
     N = batch_idx.shape[0]
-    if tuple(k_new.shape) != (N, H_kv, D) or tuple(v_new.shape) != (N, H_kv, D):
-        raise ValueError("k_new/v_new must be [N, H_kv, D]")
-    if input_pos.shape[0] != N:
-        raise ValueError("input_pos and batch_idx differ in length")
+    dv = k_pool.device
     num_slots, max_blocks = page_table.shape
     rc = L.paged_kv_append(_dev(k_pool, "k_pool", torch.bfloat16, 3),
-                           _dev(v_pool, "v_pool", torch.bfloat16, 3), rows // page_size, page_size,
-                           H_kv, D, _dev(page_table, "page_table", torch.int32, 2), num_slots,
-                           max_blocks, _dev(batch_idx, "batch_idx", torch.int32, 1),
-                           _dev(input_pos, "input_pos", torch.int32, 1), N,
-                           _dev(k_new, "k_new", torch.bfloat16, 3),
-                           _dev(v_new, "v_new", torch.bfloat16, 3), _stream(stream))
+                           _dev(v_pool, "v_pool", torch.bfloat16, 3, k_pool.shape, dv),
+                           rows // page_size, page_size, H_kv, D,
+                           _dev(page_table, "page_table", torch.int32, 2, device=dv), num_slots,
+                           max_blocks, _dev(batch_idx, "batch_idx", torch.int32, 1, device=dv),
+                           _dev(input_pos, "input_pos", torch.int32, 1, (N,), dv), N,
+                           _dev(k_new, "k_new", torch.bfloat16, 3, (N, H_kv, D), dv),
+                           _dev(v_new, "v_new", torch.bfloat16, 3, (N, H_kv, D), dv),
+                           _stream(stream))
     _check(rc, "paged_kv_append")
 
 
@@ -159,6 +171,37 @@ def paged_decode_balanced_parts(batch: int, num_kv_heads: int, max_kv_len: int) 
     return int(load_library().paged_decode_balanced_parts(batch, num_kv_heads, max_kv_len))
 
 
+def _decode_args(q, k_pool, v_pool, page_table, batch_idx, kv_len, page_size, num_splits, flags,
+                 workspace, out, lse, alloc_workspace=True):
+    """Shapes, pointers and output buffers shared by the decode wrappers."""
+    B, H_q, D = q.shape
+    H_kv, rows, D2 = k_pool.shape
+    if D2 != D or rows % page_size:
+        raise ValueError("pool shape does not match q / page_size")
+    dv = q.device
+    num_slots, max_blocks = page_table.shape
+    need = paged_decode_workspace_size(B, H_q, H_kv, D, int(num_splits), int(flags))
+    if need and workspace is None and alloc_workspace:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dv)
+    ws_ptr, ws_bytes = _workspace(workspace, dv)
+    if out is None:
+        out = torch.empty((B, H_q, D), dtype=torch.bfloat16, device=dv)
+    if lse is None:
+        lse = torch.empty((B, H_q), dtype=torch.float32, device=dv)
+    ptrs = dict(
+        q=_dev(q, "q", torch.bfloat16, 3),
+        k_pool=_dev(k_pool, "k_pool", torch.bfloat16, 3, device=dv),
+        v_pool=_dev(v_pool, "v_pool", torch.bfloat16, 3, k_pool.shape, dv),
+        page_table=_dev(page_table, "page_table", torch.int32, 2, device=dv),
+        batch_idx=_dev(batch_idx, "batch_idx", torch.int32, 1, (B,), dv),
+        kv_len=_dev(kv_len, "kv_len", torch.int32, 1, (B,), dv),
+        out=_dev(out, "out", torch.bfloat16, 3, (B, H_q, D), dv),
+        lse=_dev(lse, "lse", torch.float32, 2, (B, H_q), dv))
+    geo = dict(B=B, H_q=H_q, H_kv=H_kv, D=D, num_pages=rows // page_size, num_slots=num_slots,
+               max_blocks=max_blocks)
+    return ptrs, geo, ws_ptr, ws_bytes, out, lse
+
+
 def paged_decode_attn(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
                       page_table: torch.Tensor, batch_idx: torch.Tensor, kv_len: torch.Tensor,
                       page_size: int, scale: float, max_kv_len: int = 0, num_splits: int = 0,
@@ -174,30 +217,14 @@ def paged_decode_attn(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tenso
     here when not given and the schedule needs one.
     """
     L = load_library()
-    B, H_q, D = q.shape
-    H_kv, rows, D2 = k_pool.shape
-    if D2 != D or v_pool.shape != k_pool.shape or rows % page_size:
-        raise ValueError("pool shape does not match q / page_size")
-    num_slots, max_blocks = page_table.shape
-    if batch_idx.shape[0] != B or kv_len.shape[0] != B:
-        raise ValueError("batch_idx and kv_len must have one entry per row")
-    S = int(num_splits)
-    need = paged_decode_workspace_size(B, H_q, H_kv, D, S, int(flags))
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr, ws_bytes = (0, 0) if workspace is None else (workspace.data_ptr(), workspace.numel())
-    if out is None:
-        out = torch.empty((B, H_q, D), dtype=torch.bfloat16, device=q.device)
-    if lse is None:
-        lse = torch.empty((B, H_q), dtype=torch.float32, device=q.device)
-    rc = L.paged_decode_attn(_dev(q, "q", torch.bfloat16, 3), _dev(k_pool, "k_pool", torch.bfloat16, 3),
-                             _dev(v_pool, "v_pool", torch.bfloat16, 3), rows // page_size,
-                             page_size, H_kv, D, _dev(page_table, "page_table", torch.int32, 2),
-                             num_slots, max_blocks, _dev(batch_idx, "batch_idx", torch.int32, 1),
-                             _dev(kv_len, "kv_len", torch.int32, 1), B, H_q, float(scale),
-                             int(max_kv_len), S, int(flags), ws_ptr, ws_bytes,
-                             _dev(out, "out", torch.bfloat16, 3), _dev(lse, "lse", torch.float32, 2),
-                             _stream(stream))
+    p, g, ws_ptr, ws_bytes, out, lse = _decode_args(q, k_pool, v_pool, page_table, batch_idx,
+                                                    kv_len, page_size, num_splits, flags,
+                                                    workspace, out, lse)
+    rc = L.paged_decode_attn(p["q"], p["k_pool"], p["v_pool"], g["num_pages"], page_size,
+                             g["H_kv"], g["D"], p["page_table"], g["num_slots"], g["max_blocks"],
+                             p["batch_idx"], p["kv_len"], g["B"], g["H_q"], float(scale),
+                             int(max_kv_len), int(num_splits), int(flags), ws_ptr, ws_bytes,
+                             p["out"], p["lse"], _stream(stream))
     _check(rc, "paged_decode_attn")
     return out, lse
 
@@ -212,34 +239,54 @@ def paged_decode_attn_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.
     """Append each row's new token (k_new/v_new [B, H_kv, D], position kv_len-1) and decode,
     in one launch; returns (out, lse) as paged_decode_attn."""
     L = load_library()
-    B, H_q, D = q.shape
-    H_kv, rows, D2 = k_pool.shape
-    if D2 != D or v_pool.shape != k_pool.shape or rows % page_size:
-        raise ValueError("pool shape does not match q / page_size")
-    if tuple(k_new.shape) != (B, H_kv, D) or tuple(v_new.shape) != (B, H_kv, D):
-        raise ValueError("k_new/v_new must be [B, H_kv, D]")
-    num_slots, max_blocks = page_table.shape
-    if batch_idx.shape[0] != B or kv_len.shape[0] != B:
-        raise ValueError("batch_idx and kv_len must have one entry per row")
-    S = int(num_splits)
-    need = paged_decode_workspace_size(B, H_q, H_kv, D, S, int(flags))
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr, ws_bytes = (0, 0) if workspace is None else (workspace.data_ptr(), workspace.numel())
-    if out is None:
-        out = torch.empty((B, H_q, D), dtype=torch.bfloat16, device=q.device)
-    if lse is None:
-        lse = torch.empty((B, H_q), dtype=torch.float32, device=q.device)
+    p, g, ws_ptr, ws_bytes, out, lse = _decode_args(q, k_pool, v_pool, page_table, batch_idx,
+                                                    kv_len, page_size, num_splits, flags,
+                                                    workspace, out, lse)
+    new_shape = (g["B"], g["H_kv"], g["D"])
     rc = L.paged_decode_attn_append(
-        _dev(q, "q", torch.bfloat16, 3), _dev(k_new, "k_new", torch.bfloat16, 3),
-        _dev(v_new, "v_new", torch.bfloat16, 3), _dev(k_pool, "k_pool", torch.bfloat16, 3),
-        _dev(v_pool, "v_pool", torch.bfloat16, 3), rows // page_size, page_size, H_kv, D,
-        _dev(page_table, "page_table", torch.int32, 2), num_slots, max_blocks,
-        _dev(batch_idx, "batch_idx", torch.int32, 1), _dev(kv_len, "kv_len", torch.int32, 1), B,
-        H_q, float(scale), int(max_kv_len), S, int(flags), ws_ptr, ws_bytes,
-        _dev(out, "out", torch.bfloat16, 3), _dev(lse, "lse", torch.float32, 2), _stream(stream))
+        p["q"], _dev(k_new, "k_new", torch.bfloat16, 3, new_shape, q.device),
+        _dev(v_new, "v_new", torch.bfloat16, 3, new_shape, q.device), p["k_pool"], p["v_pool"],
+        g["num_pages"], page_size, g["H_kv"], g["D"], p["page_table"], g["num_slots"],
+        g["max_blocks"], p["batch_idx"], p["kv_len"], g["B"], g["H_q"], float(scale),
+        int(max_kv_len), int(num_splits), int(flags), ws_ptr, ws_bytes, p["out"], p["lse"],
+        _stream(stream))
     _check(rc, "paged_decode_attn_append")
     return out, lse
+
+
+def _prefill_args(q, k, v, cu_seqlens, out, lse):
+    """Shapes, pointers and output buffers shared by the prefill wrappers."""
+    Lt, H_q, D = q.shape
+    H_kv = k.shape[1] if k.dim() == 3 else 0
+    dv = q.device
+    n_docs = cu_seqlens.shape[0] - 1
+    if out is None:
+        out = torch.empty((Lt, H_q, D), dtype=torch.bfloat16, device=dv)
+    if lse is None:
+        lse = torch.empty((Lt, H_q), dtype=torch.float32, device=dv)
+    ptrs = dict(
+        q=_dev(q, "q", torch.bfloat16, 3),
+        k=_dev(k, "k", torch.bfloat16, 3, (Lt, H_kv, D), dv),
+        v=_dev(v, "v", torch.bfloat16, 3, (Lt, H_kv, D), dv),
+        cu_seqlens=_dev(cu_seqlens, "cu_seqlens", torch.int32, 1, device=dv),
+        out=_dev(out, "out", torch.bfloat16, 3, (Lt, H_q, D), dv),
+        lse=_dev(lse, "lse", torch.float32, 2, (Lt, H_q), dv))
+    geo = dict(L=Lt, H_q=H_q, H_kv=H_kv, D=D, n_docs=n_docs)
+    return ptrs, geo, out, lse
+
+
+def _pool_args(k_pool, v_pool, page_table, page_size, H_kv, D, device):
+    """Pointers and sizes of the paged pools the fused prefill calls write."""
+    if k_pool.dim() != 3:
+        raise ValueError("k_pool must be [H_kv, num_pages*page_size, D]")
+    Hp, rows, Dp = k_pool.shape
+    if Hp != H_kv or Dp != D or rows % page_size:
+        raise ValueError("pool shape does not match k / page_size")
+    num_slots, max_blocks = page_table.shape
+    ptrs = dict(k_pool=_dev(k_pool, "k_pool", torch.bfloat16, 3, device=device),
+                v_pool=_dev(v_pool, "v_pool", torch.bfloat16, 3, k_pool.shape, device),
+                page_table=_dev(page_table, "page_table", torch.int32, 2, device=device))
+    return ptrs, dict(num_pages=rows // page_size, num_slots=num_slots, max_blocks=max_blocks)
 
 
 def packed_prefill_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
@@ -248,20 +295,10 @@ def packed_prefill_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                         stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Document-causal prefill; returns (out bf16 [L, H_q, D], lse fp32 [L, H_q])."""
     L = load_library()
-    Lt, H_q, D = q.shape
-    _, H_kv, _ = k.shape
-    if tuple(k.shape) != (Lt, H_kv, D) or tuple(v.shape) != (Lt, H_kv, D):
-        raise ValueError("k/v must be [L, H_kv, D] matching q")
-    n_docs = cu_seqlens.shape[0] - 1
-    if out is None:
-        out = torch.empty((Lt, H_q, D), dtype=torch.bfloat16, device=q.device)
-    if lse is None:
-        lse = torch.empty((Lt, H_q), dtype=torch.float32, device=q.device)
-    rc = L.packed_prefill_attn(_dev(q, "q", torch.bfloat16, 3), _dev(k, "k", torch.bfloat16, 3),
-                               _dev(v, "v", torch.bfloat16, 3),
-                               _dev(cu_seqlens, "cu_seqlens", torch.int32, 1), n_docs, Lt, H_q,
-                               H_kv, D, float(scale), _dev(out, "out", torch.bfloat16, 3),
-                               _dev(lse, "lse", torch.float32, 2), _stream(stream))
+    p, g, out, lse = _prefill_args(q, k, v, cu_seqlens, out, lse)
+    rc = L.packed_prefill_attn(p["q"], p["k"], p["v"], p["cu_seqlens"], g["n_docs"], g["L"],
+                               g["H_q"], g["H_kv"], g["D"], float(scale), p["out"], p["lse"],
+                               _stream(stream))
     _check(rc, "packed_prefill_attn")
     return out, lse
 
@@ -276,29 +313,13 @@ def packed_prefill_attn_append(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
     """Document-causal prefill plus the scatter of each document's K/V (slot doc_slots[d],
     positions 0..n_d-1) into the pools, in one launch; returns (out, lse)."""
     L = load_library()
-    Lt, H_q, D = q.shape
-    _, H_kv, _ = k.shape
-    if tuple(k.shape) != (Lt, H_kv, D) or tuple(v.shape) != (Lt, H_kv, D):
-        raise ValueError("k/v must be [L, H_kv, D] matching q")
-    Hp, rows, Dp = k_pool.shape
-    if Hp != H_kv or Dp != D or v_pool.shape != k_pool.shape or rows % page_size:
-        raise ValueError("pool shape does not match k / page_size")
-    n_docs = cu_seqlens.shape[0] - 1
-    if doc_slots.shape[0] != n_docs:
-        raise ValueError("doc_slots must have one entry per document")
-    num_slots, max_blocks = page_table.shape
-    if out is None:
-        out = torch.empty((Lt, H_q, D), dtype=torch.bfloat16, device=q.device)
-    if lse is None:
-        lse = torch.empty((Lt, H_q), dtype=torch.float32, device=q.device)
+    p, g, out, lse = _prefill_args(q, k, v, cu_seqlens, out, lse)
+    pp, pg = _pool_args(k_pool, v_pool, page_table, page_size, g["H_kv"], g["D"], q.device)
     rc = L.packed_prefill_attn_append(
-        _dev(q, "q", torch.bfloat16, 3), _dev(k, "k", torch.bfloat16, 3),
-        _dev(v, "v", torch.bfloat16, 3), _dev(cu_seqlens, "cu_seqlens", torch.int32, 1), n_docs,
-        Lt, H_q, H_kv, D, float(scale), _dev(out, "out", torch.bfloat16, 3),
-        _dev(lse, "lse", torch.float32, 2), _dev(k_pool, "k_pool", torch.bfloat16, 3),
-        _dev(v_pool, "v_pool", torch.bfloat16, 3), rows // page_size, page_size,
-        _dev(page_table, "page_table", torch.int32, 2), num_slots, max_blocks,
-        _dev(doc_slots, "doc_slots", torch.int32, 1), _stream(stream))
+        p["q"], p["k"], p["v"], p["cu_seqlens"], g["n_docs"], g["L"], g["H_q"], g["H_kv"],
+        g["D"], float(scale), p["out"], p["lse"], pp["k_pool"], pp["v_pool"], pg["num_pages"],
+        page_size, pp["page_table"], pg["num_slots"], pg["max_blocks"],
+        _dev(doc_slots, "doc_slots", torch.int32, 1, (g["n_docs"],), q.device), _stream(stream))
     _check(rc, "packed_prefill_attn_append")
     return out, lse
 
@@ -312,30 +333,15 @@ def paged_prefill_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seq
     """Chunked prefill: chunk rows attend to their sequence's cached prefix (pages) and to
     the chunk causally; the chunk's K/V are written into the pages.  Returns (out, lse)."""
     L = load_library()
-    Lt, H_q, D = q.shape
-    _, H_kv, _ = k.shape
-    if tuple(k.shape) != (Lt, H_kv, D) or tuple(v.shape) != (Lt, H_kv, D):
-        raise ValueError("k/v must be [L, H_kv, D] matching q")
-    Hp, rows, Dp = k_pool.shape
-    if Hp != H_kv or Dp != D or v_pool.shape != k_pool.shape or rows % page_size:
-        raise ValueError("pool shape does not match k / page_size")
-    n_docs = cu_seqlens.shape[0] - 1
-    if doc_slots.shape[0] != n_docs or prefix_lens.shape[0] != n_docs:
-        raise ValueError("doc_slots and prefix_lens must have one entry per document")
-    num_slots, max_blocks = page_table.shape
-    if out is None:
-        out = torch.empty((Lt, H_q, D), dtype=torch.bfloat16, device=q.device)
-    if lse is None:
-        lse = torch.empty((Lt, H_q), dtype=torch.float32, device=q.device)
+    p, g, out, lse = _prefill_args(q, k, v, cu_seqlens, out, lse)
+    pp, pg = _pool_args(k_pool, v_pool, page_table, page_size, g["H_kv"], g["D"], q.device)
+    nd = (g["n_docs"],)
     rc = L.paged_prefill_attn(
-        _dev(q, "q", torch.bfloat16, 3), _dev(k, "k", torch.bfloat16, 3),
-        _dev(v, "v", torch.bfloat16, 3), _dev(cu_seqlens, "cu_seqlens", torch.int32, 1),
-        _dev(prefix_lens, "prefix_lens", torch.int32, 1),
-        _dev(doc_slots, "doc_slots", torch.int32, 1), n_docs, Lt, H_q, H_kv, D, float(scale),
-        _dev(k_pool, "k_pool", torch.bfloat16, 3), _dev(v_pool, "v_pool", torch.bfloat16, 3),
-        rows // page_size, page_size, _dev(page_table, "page_table", torch.int32, 2), num_slots,
-        max_blocks, _dev(out, "out", torch.bfloat16, 3), _dev(lse, "lse", torch.float32, 2),
-        _stream(stream))
+        p["q"], p["k"], p["v"], p["cu_seqlens"],
+        _dev(prefix_lens, "prefix_lens", torch.int32, 1, nd, q.device),
+        _dev(doc_slots, "doc_slots", torch.int32, 1, nd, q.device), g["n_docs"], g["L"], g["H_q"],
+        g["H_kv"], g["D"], float(scale), pp["k_pool"], pp["v_pool"], pg["num_pages"], page_size,
+        pp["page_table"], pg["num_slots"], pg["max_blocks"], p["out"], p["lse"], _stream(stream))
     _check(rc, "paged_prefill_attn")
     return out, lse
 
@@ -347,15 +353,15 @@ def validate_decode(page_table: torch.Tensor, batch_idx: torch.Tensor, kv_len: t
     (violating rows, first violating row or -1, its PKV_V_* code, block or -1)."""
     L = load_library()
     B = batch_idx.shape[0]
-    if kv_len.shape[0] != B:
-        raise ValueError("kv_len and batch_idx differ in length")
+    dv = batch_idx.device
     num_slots, max_blocks = page_table.shape
     if report is None:
-        report = torch.empty(4, dtype=torch.int32, device=batch_idx.device)
-    rc = L.pkv_validate_decode(_dev(page_table, "page_table", torch.int32, 2), num_pages, page_size,
-                               num_slots, max_blocks, _dev(batch_idx, "batch_idx", torch.int32, 1),
-                               _dev(kv_len, "kv_len", torch.int32, 1), B,
-                               _dev(report, "report", torch.int32, 1), _stream(stream))
+        report = torch.empty(4, dtype=torch.int32, device=dv)
+    rc = L.pkv_validate_decode(_dev(page_table, "page_table", torch.int32, 2, device=dv),
+                               num_pages, page_size, num_slots, max_blocks,
+                               _dev(batch_idx, "batch_idx", torch.int32, 1),
+                               _dev(kv_len, "kv_len", torch.int32, 1, (B,), dv), B,
+                               _dev(report, "report", torch.int32, 1, (4,), dv), _stream(stream))
     _check(rc, "pkv_validate_decode")
     return report
 
@@ -371,16 +377,17 @@ def validate_prefill(cu_seqlens: torch.Tensor, total_len: int,
     block or -1)."""
     L = load_library()
     n_docs = cu_seqlens.shape[0] - 1
+    dv = cu_seqlens.device
     num_slots, max_blocks = page_table.shape if page_table is not None else (1, 1)
-    for t, name in ((doc_slots, "doc_slots"), (prefix_lens, "prefix_lens")):
-        if t is not None and t.shape[0] != n_docs:
-            raise ValueError(f"{name} must have one entry per document")
     if report is None:
-        report = torch.empty(4, dtype=torch.int32, device=cu_seqlens.device)
-    opt = lambda t, name, nd: _dev(t, name, torch.int32, nd) if t is not None else None  # noqa: E731
+        report = torch.empty(4, dtype=torch.int32, device=dv)
+    opt = lambda t, name, nd, shp: (  # noqa: E731
+        _dev(t, name, torch.int32, nd, shp, dv) if t is not None else None)
     rc = L.pkv_validate_prefill(_dev(cu_seqlens, "cu_seqlens", torch.int32, 1), n_docs, total_len,
-                                opt(doc_slots, "doc_slots", 1), opt(prefix_lens, "prefix_lens", 1),
-                                opt(page_table, "page_table", 2), num_pages, page_size, num_slots,
-                                max_blocks, _dev(report, "report", torch.int32, 1), _stream(stream))
+                                opt(doc_slots, "doc_slots", 1, (n_docs,)),
+                                opt(prefix_lens, "prefix_lens", 1, (n_docs,)),
+                                opt(page_table, "page_table", 2, None), num_pages, page_size,
+                                num_slots, max_blocks,
+                                _dev(report, "report", torch.int32, 1, (4,), dv), _stream(stream))
     _check(rc, "pkv_validate_prefill")
     return report

@@ -3,7 +3,8 @@ acceptance check against the float64 reference.
 
 Acceptance (stated for this path): bf16 outputs within
 |gpu - ref| <= 1.6e-2 + 1e-2 * |ref| elementwise, |delta LSE| <= 1e-3, an
-LSE of -inf reproduced exactly, no NaN anywhere.
+LSE of -inf reproduced exactly together with an output of exactly +0.0 for
+that (row, head), no NaN anywhere.
 """
 from __future__ import annotations
 
@@ -30,6 +31,13 @@ def host_bits(t: torch.Tensor) -> np.ndarray:
     return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+def assert_padding_exact(out_gpu: torch.Tensor, lse_gpu: torch.Tensor, what: str = "") -> None:
+    """Rows with no valid key: every output bit pattern is +0.0 and every LSE is -inf."""
+    assert not host_bits(out_gpu).any(), f"{what}: padding output is not exactly +0.0"
+    l = lse_gpu.detach().cpu().numpy()
+    assert np.isneginf(l).all(), f"{what}: padding LSE is not -inf"
+
+
 def host_f64(t: torch.Tensor) -> np.ndarray:
     if t.dtype == torch.bfloat16:
         return bf16_bits_to_f32(host_bits(t)).astype(np.float64)
@@ -53,6 +61,15 @@ def check_close(out_gpu: torch.Tensor, lse_gpu: torch.Tensor, out_ref: np.ndarra
                              f"{idx.tolist()}: gpu {o[tuple(idx[0])]} ref {out_ref[tuple(idx[0])]}")
     ninf_ref = np.isneginf(lse_ref)
     assert np.array_equal(np.isneginf(l), ninf_ref), f"{what}: -inf LSE pattern differs"
+    if ninf_ref.any():
+        # A (row, head) with no valid key returns exactly +0.0 (bit pattern 0), not merely
+        # something inside the tolerance band.
+        bits = host_bits(out_gpu) if out_gpu.dtype == torch.bfloat16 else None
+        if bits is not None:
+            assert not bits[ninf_ref].any(), f"{what}: a row without keys is not exactly +0.0"
+        else:
+            assert (o[ninf_ref] == 0).all() and not np.signbit(o[ninf_ref]).any(), \
+                f"{what}: a row without keys is not exactly +0.0"
     fin = ~ninf_ref
     lerr = np.abs(l[fin] - lse_ref[fin])
     assert (lerr <= LSE_TOL).all(), f"{what}: LSE error {lerr.max()}"

@@ -17,7 +17,7 @@ if not torch.cuda.is_available():  # pragma: no cover
 
 import paged_kv_attention_23_amd as pkv  # noqa: E402
 from paged_kv_attention_23_amd.graphs import DecodeGraphs  # noqa: E402
-from gpu_util import check_close, dev_bf16, dev_i32, host_bits  # noqa: E402
+from gpu_util import assert_padding_exact, check_close, dev_bf16, dev_i32, host_bits  # noqa: E402
 
 
 def _case(seed, B, ps=128):
@@ -78,6 +78,8 @@ def test_decode_graphs_buckets(schedule):
             assert torch.equal(out.view(torch.int16), eo.view(torch.int16)), (n, rep)
             assert torch.equal(lse, el), (n, rep)
             check_close(out, lse, out_ref, lse_ref, f"graphs n={n} rep={rep}")
+            if b > n:  # the bucket's padding rows (slot 0): exactly (+0, -inf)
+                assert_padding_exact(runner.out[n:b], runner.lse[n:b], f"graphs pad n={n}")
             _ = (torch.ones(1 << 20, device="cuda") * 2).sum().item()  # eager work between replays
     # the pools hold exactly the oracle's appended tokens (appends are idempotent)
     assert np.array_equal(host_bits(kd), kp_ref) and np.array_equal(host_bits(vd), vp_ref)
