@@ -11,10 +11,20 @@ A step is one pass of the hot path over one batch of synthetic input:
            L ~ 18k), as one packed_prefill_attn_append launch (--separate:
            paged_kv_append, then packed_prefill_attn).
 
+Beside the headline step, every named workload gets its own entry under
+"configs" (tiny decode; B=8 decode + append; the B=64 bucket, with the
+contiguous-page path against the page-table walk; B=256 through the
+automatic plan, split-K + merge and the balanced schedule; packed prefill),
+each timed cold and warm, plus the float64 oracle timed on the host cores
+(all threads, and one thread for the decode workloads).  "ceilings" holds
+what plain kernels of the same shapes reach on this GPU: a streaming read,
+a streaming read with the decode launch shape, a dense bf16 matrix-core
+loop and a library bf16 GEMM.
+
 Cold data without a flush: like the layers of a model, the benchmark keeps
 several independent KV caches (and prefill inputs) and runs the steps back to
 back, rotating through them, so every call reads data that was last touched
-several calls (>1 GiB of other traffic) earlier and cannot still sit in the
+more than 512 MB of other traffic earlier and cannot still sit in the
 256 MiB Infinity Cache.  The K timed steps are captured into one HIP graph
 (as a serving loop captures its decode step per batch bucket, the pages'
 CUDA-graph setup) and replayed once, bracketed by one pair of HIP events on
@@ -28,8 +38,10 @@ Prints one JSON line.  value = decode KV bytes per step / decode step time
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -44,6 +56,8 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak, published
 METRIC = "paged decode KV-read GB/s (% of HBM peak) at B=64; prefill TFLOP/s"
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "paged_kv_attention_23_amd", "csrc")
+CEIL_LIB = os.path.join(ROOT, "paged_kv_attention_23_amd", "measure", "libpkvceil.so")
+COLD_DISTANCE = 600e6          # bytes of other traffic between two reads of the same data
 
 
 def parse():
@@ -52,7 +66,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--layers", type=int, default=8,
-                    help="independent KV caches rotated through by the decode steps")
+                    help="independent KV caches rotated through by the headline decode steps")
     ap.add_argument("--prefill-layers", type=int, default=4,
                     help="independent prefill input sets rotated through")
     ap.add_argument("--num-splits", type=int, default=0,
@@ -68,8 +82,13 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-chunked", action="store_true",
                     help="skip the chunked-prefill (paged prefix) measurement")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="budget for the CPU oracle baseline (0 = skip)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload entries (configs 1, 2 and 4; the B=64 path A/B)")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the reachable-rate probes")
+    ap.add_argument("--only", choices=["decode", "prefill"], default=None,
+                    help="time only the decode or only the prefill attention call (profiling runs)")
+    ap.add_argument("--cpu-seconds", type=float, default=2.0,
+                    help="budget per oracle measurement on the host (0 = skip)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (counter calibration)")
     return ap.parse_args()
@@ -109,6 +128,343 @@ def measured_traffic(kernel: str, source: str):
     return int(t["traffic_bytes"]) if t.get("source_sha256") == sha else None
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+class Timer:
+    """Device time of fn(0..n-1) on the current stream (graph-replayed unless eager/flush)."""
+
+    def __init__(self, torch, stream, args, dev):
+        self.torch, self.stream, self.args = torch, stream, args
+        self.flush_buf = torch.ones(1024 * 1024 * 1024 // 4, dtype=torch.float32, device=dev) \
+            if args.flush else None
+        self.flush_sink = torch.empty((), dtype=torch.float32, device=dev)
+
+    def events(self):
+        t = self.torch
+        return t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+
+    def __call__(self, fn, n, replays=None):
+        """Total ms of n steps.  With a list `replays`, the captured graph is replayed 5
+        more times and each replay's total (ms) is appended to it."""
+        torch, stream, args = self.torch, self.stream, self.args
+        if args.flush:  # each call alone after a 1 GiB read (clean eviction)
+            total = 0.0
+            for i in range(n):
+                torch.sum(self.flush_buf, dim=0, out=self.flush_sink)
+                e0, e1 = self.events()
+                e0.record(stream)
+                fn(i)
+                e1.record(stream)
+                e1.synchronize()
+                total += e0.elapsed_time(e1)
+            return total
+        if args.eager:
+            torch.cuda.synchronize()
+            e0, e1 = self.events()
+            e0.record(stream)
+            for i in range(n):
+                fn(i)
+            e1.record(stream)
+            e1.synchronize()
+            return e0.elapsed_time(e1)
+        # The n steps are captured once into a HIP graph (as a serving loop
+        # captures its decode step) and replayed: the timed region holds the
+        # GPU work only, not Python's per-call launch cost.  All buffers are
+        # allocated before the capture; no memset is recorded.
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(n):
+                fn(i)
+        graph.replay()                      # first replay uploads the graph
+        torch.cuda.synchronize()
+        e0, e1 = self.events()
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        e1.synchronize()
+        total = e0.elapsed_time(e1)
+        if replays is not None:
+            for _ in range(5):
+                e0.record(stream)
+                graph.replay()
+                e1.record(stream)
+                e1.synchronize()
+                replays.append(e0.elapsed_time(e1))
+        del graph
+        return total
+
+
+def layers_for(nbytes: float, cap: int = 64) -> int:
+    """Independent copies needed so that COLD_DISTANCE bytes pass between two reuses."""
+    return int(min(cap, max(2, math.ceil(COLD_DISTANCE / max(nbytes, 1.0)) + 1)))
+
+
+class DecodeBench:
+    """One decode workload on the GPU: NL independent pool copies, rotated through."""
+
+    def __init__(self, torch, pkv, case, dev, layers=None):
+        from gpu_util import dev_bf16, dev_i32
+        self.torch, self.pkv, self.c = torch, pkv, case
+        c = case
+        self.kv_bytes = c.kv_bytes()
+        self.NL = layers if layers else layers_for(self.kv_bytes)
+        k0, v0 = dev_bf16(c.k_pool), dev_bf16(c.v_pool)
+        self.k = [k0] + [k0.clone() for _ in range(self.NL - 1)]
+        self.v = [v0] + [v0.clone() for _ in range(self.NL - 1)]
+        self.q = dev_bf16(c.q)
+        self.pt, self.bi, self.kl = dev_i32(c.page_table), dev_i32(c.batch_idx), dev_i32(c.kv_len)
+        self.max_kv = int(c.kv_len.max())
+        self.out = torch.empty((c.B, c.H_q, c.D), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((c.B, c.H_q), dtype=torch.float32, device=dev)
+        self.ws = {}
+        self.dev = dev
+        act = c.active_rows()
+        self.act = act
+        rng = np.random.default_rng(9303 + c.seed)
+        from workloads import f32_to_bf16_bits
+        row_k = np.zeros((c.B, c.H_kv, c.D), np.uint16)
+        row_v = np.zeros_like(row_k)
+        row_k[act] = f32_to_bf16_bits(rng.standard_normal((len(act), c.H_kv, c.D), dtype=np.float32))
+        row_v[act] = f32_to_bf16_bits(rng.standard_normal((len(act), c.H_kv, c.D), dtype=np.float32))
+        self.rk, self.rv = dev_bf16(row_k), dev_bf16(row_v)
+
+    def workspace(self, S, flags):
+        key = (S, flags)
+        if key not in self.ws:
+            c = self.c
+            n = self.pkv.paged_decode_workspace_size(c.B, c.H_q, c.H_kv, c.D, S, flags)
+            self.ws[key] = self.torch.empty(max(n, 16), dtype=self.torch.uint8, device=self.dev)
+        return self.ws[key]
+
+    def call(self, S=0, flags=0, rotate=True):
+        c, pkv = self.c, self.pkv
+        ws = self.workspace(S, flags)
+
+        def fn(i):
+            j = i % self.NL if rotate else 0
+            pkv.paged_decode_attn(self.q, self.k[j], self.v[j], self.pt, self.bi, self.kl,
+                                  page_size=c.page_size, scale=float(c.scale),
+                                  max_kv_len=self.max_kv, num_splits=S, flags=flags,
+                                  workspace=ws, out=self.out, lse=self.lse)
+        return fn
+
+    def fused(self, S=0, flags=0):
+        c, pkv = self.c, self.pkv
+        ws = self.workspace(S, flags)
+
+        def fn(i):
+            j = i % self.NL
+            pkv.paged_decode_attn_append(self.q, self.rk, self.rv, self.k[j], self.v[j], self.pt,
+                                         self.bi, self.kl, page_size=c.page_size,
+                                         scale=float(c.scale), max_kv_len=self.max_kv,
+                                         num_splits=S, flags=flags, workspace=ws, out=self.out,
+                                         lse=self.lse)
+        return fn
+
+    def free(self):
+        self.k = self.v = None
+        self.ws = {}
+
+
+def plan_name(pkv, c, S, flags, max_kv):
+    if flags & pkv.PKV_F_BALANCED or (S == 0 and max_kv > 2048):
+        W = pkv.paged_decode_balanced_parts(c.B, c.H_kv, max_kv)
+        return f"balanced: {W} workgroups per KV head", 1, W
+    s = S or pkv.paged_decode_num_splits(c.B, c.H_kv, max_kv)
+    return f"per-row: {s} split(s) per row", s, 0
+
+
+def time_decode(timer, db, K, S=0, flags=0, warm=True, replays=False):
+    """Cold (rotating copies) and warm (one copy) per-call times of one decode plan."""
+    reps = [] if replays else None
+    cold_ms = timer(db.call(S, flags), K, reps) / K
+    r = {"cold_us": round(cold_ms * 1e3, 3),
+         "gbs": round(db.kv_bytes / (cold_ms * 1e-3) / 1e9, 2),
+         "frac_of_hbm_peak": round(db.kv_bytes / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    if reps:
+        r["replays_us"] = {"median": round(float(np.median(reps)) / K * 1e3, 3),
+                           "best": round(min(reps) / K * 1e3, 3), "n": len(reps)}
+    if warm:
+        warm_ms = timer(db.call(S, flags, rotate=False), K) / K
+        r["warm_us"] = round(warm_ms * 1e3, 3)
+    return r, cold_ms
+
+
+def oracle_rate(fn, units, budget_s, threads=None):
+    """Repeat the oracle call until budget_s has passed (at least once); units per second."""
+    import oracle
+    prev = oracle.num_threads()
+    if threads:
+        oracle.set_threads(threads)
+    try:
+        used = oracle.num_threads()
+        reps, total = 0, 0.0
+        while total < budget_s or reps == 0:
+            t0 = time.perf_counter()
+            fn()
+            total += time.perf_counter() - t0
+            reps += 1
+    finally:
+        oracle.set_threads(prev)
+    return units * reps / total, used, reps, total
+
+
+def cpu_decode_baseline(c, budget_s, single=True):
+    import oracle
+    lo = np.zeros(c.B, np.int32)
+    kvb = c.kv_bytes()
+
+    def fn():
+        oracle.decode(c.q, c.k_pool, c.v_pool, c.num_pages, c.page_size, c.page_table,
+                      c.batch_idx, lo, c.kv_len, c.scale)
+    gbs, cores, reps, t = oracle_rate(fn, kvb / 1e9, budget_s)
+    r = {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+         "sample": f"the whole decode call ({kvb / 1e6:.1f} MB of KV), {reps}x in {t:.2f} s"}
+    if single:
+        g1, _, reps1, t1 = oracle_rate(fn, kvb / 1e9, budget_s, threads=1)
+        r["one_thread"] = {"value": round(g1, 4), "unit": "GB/s", "cores": 1,
+                           "sample": f"{reps1}x in {t1:.2f} s"}
+    return r
+
+
+def cpu_prefill_baseline(pc, budget_s):
+    import oracle
+    flops = pc.flops()
+    docs = min(pc.n_docs, 16)  # a bounded sample: the first documents of the packing
+    cu = pc.cu_seqlens[:docs + 1].astype(np.int32)
+    end = int(cu[-1])
+    n = np.diff(cu.astype(np.int64))
+    sflops = 4 * pc.D * pc.H_q * int((n * (n + 1) // 2).sum())
+
+    def fn():
+        oracle.prefill(pc.q[:end], pc.k[:end], pc.v[:end], cu, pc.scale)
+    gf, cores, reps, t = oracle_rate(fn, sflops / 1e9, budget_s)
+    return {"value": round(gf / 1e3, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"the first {docs} of the {pc.n_docs} documents ({end} rows, "
+                      f"{sflops / 1e9:.2f} of the call's {flops / 1e9:.1f} GFLOP), "
+                      f"{reps}x in {t:.2f} s"}
+
+
+def load_ceil():
+    if not os.path.exists(CEIL_LIB):
+        return None
+    L = ctypes.CDLL(CEIL_LIB)
+    L.ceil_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int,
+                                   ctypes.c_void_p, ctypes.c_void_p]
+    L.ceil_stream_units.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int,
+                                    ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    L.ceil_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    return L
+
+
+def ceilings(torch, timer, dev, db3, K):
+    """What plain kernels of the attention kernels' shapes reach on this GPU."""
+    L = load_ceil()
+    out = {}
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+
+    def st():  # the stream current at call time (a capture stream inside a graph capture)
+        return torch.cuda.current_stream().cuda_stream
+
+    sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+    if L is not None:
+        big = torch.ones(2 * 1024 ** 3 // 4, dtype=torch.float32, device=dev)
+        nb = big.numel() * 4
+        best = None
+        for grid in (cus * 4, cus * 8, cus * 16):
+            def fn(i, grid=grid):
+                assert L.ceil_stream_read(big.data_ptr(), nb, grid, sink.data_ptr(), st()) == 0
+            ms = timer(fn, 4) / 4
+            gbs = nb / (ms * 1e-3) / 1e9
+            if best is None or gbs > best[0]:
+                best = (gbs, grid, ms)
+        out["stream_read"] = {"gbs": round(best[0], 1), "bytes": nb, "grid": best[1],
+                              "us": round(best[2] * 1e3, 2),
+                              "frac_of_hbm_peak": round(best[0] / HBM_PEAK_GBS, 4),
+                              "kernel": "grid-strided non-temporal 16-byte loads, 256 threads"}
+        # the same bytes as one B=64 decode call, in windows of a 2 GiB buffer read in turn
+        w = (db3.kv_bytes + 255) // 256 * 256
+        nwin = nb // w
+
+        def fw(i):
+            off = (i % nwin) * w
+            assert L.ceil_stream_read(big.data_ptr() + off, w, best[1], sink.data_ptr(), st()) == 0
+        ms = timer(fw, K) / K
+        out["stream_read_decode_bytes"] = {
+            "us": round(ms * 1e3, 3), "bytes": int(w), "gbs": round(w / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(w / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "note": "one grid-strided read of as many bytes as the B=64 decode call, cold"}
+        del big
+        # the decode launch shape, streaming only: one unit per (row, KV head), its K and V
+        # rows a contiguous run (the workload's sequential pages), 4 waves, one 32-key tile
+        # in flight per wave; padding rows have no keys
+        c = db3.c
+        if c.contiguous:
+            units = np.zeros((c.B * c.H_kv, 2), np.int32)
+            plane_rows = c.num_pages * c.page_size
+            for r in range(c.B):
+                s, n = int(c.batch_idx[r]), int(c.kv_len[r])
+                if s == 0 or n <= 0:
+                    continue
+                row0 = int(c.page_table[s, 0]) * c.page_size
+                assert 0 <= row0 and row0 + n <= plane_rows
+                units[r * c.H_kv:(r + 1) * c.H_kv] = (row0, n)
+            du = torch.from_numpy(units.reshape(-1)).to(dev)
+            plane_bytes = plane_rows * c.D * 2
+
+            def fu(i):
+                j = i % db3.NL
+                assert L.ceil_stream_units(db3.k[j].data_ptr(), db3.v[j].data_ptr(), plane_bytes,
+                                           c.H_kv, du.data_ptr(), c.B * c.H_kv, sink.data_ptr(),
+                                           st()) == 0
+            ms = timer(fu, K) / K
+            out["decode_shape_stream"] = {
+                "us": round(ms * 1e3, 3), "bytes": int(db3.kv_bytes),
+                "gbs": round(db3.kv_bytes / (ms * 1e-3) / 1e9, 1),
+                "frac_of_hbm_peak": round(db3.kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "note": "the B=64 decode's launch shape and bytes with no arithmetic: "
+                        f"{c.B * c.H_kv} workgroups of 4 waves (one per row and KV head), cold"}
+        fsink = torch.zeros(1024, dtype=torch.float32, device=dev)
+        iters, grid = 4000, 2 * cus
+
+        def fm(i):
+            assert L.ceil_mfma(grid, iters, fsink.data_ptr(), st()) == 0
+        ms = timer(fm, 4) / 4
+        flops = grid * 4 * iters * 16 * (16 * 16 * 32 * 2)
+        out["mfma_bf16"] = {"tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                            "frac_of_peak": round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                            "kernel": "v_mfma_f32_16x16x32_bf16, 16 independent accumulators "
+                                      "per wave, 2 waves per SIMD"}
+    n = 8192
+    a = torch.randn((n, n), dtype=torch.bfloat16, device=dev)
+    b = torch.randn((n, n), dtype=torch.bfloat16, device=dev)
+    cbuf = torch.empty((n, n), dtype=torch.bfloat16, device=dev)
+    for _ in range(2):
+        torch.matmul(a, b, out=cbuf)
+    torch.cuda.synchronize()
+    e0, e1 = timer.events()
+    e0.record()
+    for _ in range(5):
+        torch.matmul(a, b, out=cbuf)
+    e1.record()
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    out["torch_matmul_bf16"] = {"tflops": round(2 * n ** 3 / (ms * 1e-3) / 1e12, 1),
+                                "shape": [n, n, n],
+                                "frac_of_peak": round(2 * n ** 3 / (ms * 1e-3) / 1e12
+                                                      / BF16_PEAK_TFLOPS, 4)}
+    return out
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -122,7 +478,7 @@ def main():
     import torch
 
     import paged_kv_attention_23_amd as pkv
-    from workloads import f32_to_bf16_bits, make_case
+    from workloads import make_case
 
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from gpu_util import dev_bf16, dev_i32
@@ -131,52 +487,31 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+    timer = Timer(torch, stream, args, dev)
+    K = args.steps
+
+    def progress(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
     # ---------------- decode inputs (bucketed B=64), one KV cache per layer
     c = make_case(3, fill="zero")
-    rng = np.random.default_rng(9303)
-    act = c.active_rows()
-    app_bi = c.batch_idx[act].astype(np.int32)
-    app_pos = (c.kv_len[act] - 1).astype(np.int32)         # the step's new token is key n-1
-    app_k = f32_to_bf16_bits(rng.standard_normal((len(act), c.H_kv, c.D), dtype=np.float32))
-    app_v = f32_to_bf16_bits(rng.standard_normal((len(act), c.H_kv, c.D), dtype=np.float32))
-    d_q = dev_bf16(c.q)
-    k0, v0 = dev_bf16(c.k_pool), dev_bf16(c.v_pool)
-    NL = max(1, args.layers)
-    d_k = [k0] + [k0.clone() for _ in range(NL - 1)]
-    d_v = [v0] + [v0.clone() for _ in range(NL - 1)]
-    d_pt, d_bi, d_kl = dev_i32(c.page_table), dev_i32(c.batch_idx), dev_i32(c.kv_len)
-    d_abi, d_apos = dev_i32(app_bi), dev_i32(app_pos)
-    d_ak, d_av = dev_bf16(app_k), dev_bf16(app_v)
-    row_k = np.zeros((c.B, c.H_kv, c.D), np.uint16)   # the same tokens, indexed by row
-    row_v = np.zeros_like(row_k)
-    row_k[act], row_v[act] = app_k, app_v
-    d_rk, d_rv = dev_bf16(row_k), dev_bf16(row_v)
-    max_kv = int(c.kv_len.max())
+    db = DecodeBench(torch, pkv, c, dev, layers=max(1, args.layers))
     balanced = bool(args.flags & pkv.PKV_F_BALANCED)
-    S = args.num_splits or (0 if balanced else pkv.paged_decode_num_splits(c.B, c.H_kv, max_kv))
-    W = pkv.paged_decode_balanced_parts(c.B, c.H_kv, max_kv) if balanced else 0
-    ws_bytes = pkv.paged_decode_workspace_size(c.B, c.H_q, c.H_kv, c.D, S, args.flags)
-    d_ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    d_out = torch.empty((c.B, c.H_q, c.D), dtype=torch.bfloat16, device=dev)
-    d_lse = torch.empty((c.B, c.H_q), dtype=torch.float32, device=dev)
-    kv_bytes = c.kv_bytes()
-
-    def decode_only(i):
-        pkv.paged_decode_attn(d_q, d_k[i % NL], d_v[i % NL], d_pt, d_bi, d_kl,
-                              page_size=c.page_size, scale=float(c.scale), max_kv_len=max_kv,
-                              num_splits=S, flags=args.flags, workspace=d_ws, out=d_out, lse=d_lse)
+    sched, S_eff, W = plan_name(pkv, c, args.num_splits, args.flags, db.max_kv)
+    S = args.num_splits
+    kv_bytes = db.kv_bytes
+    app_bi = dev_i32(c.batch_idx[db.act].astype(np.int32))
+    app_pos = dev_i32((c.kv_len[db.act] - 1).astype(np.int32))
+    app_k = db.rk[torch.from_numpy(db.act).to(dev)].contiguous()
+    app_v = db.rv[torch.from_numpy(db.act).to(dev)].contiguous()
+    decode_only = db.call(S, args.flags)
+    decode_step_fused = db.fused(S, args.flags)
 
     def decode_step_separate(i):
-        pkv.paged_kv_append(d_k[i % NL], d_v[i % NL], d_pt, d_abi, d_apos, d_ak, d_av,
+        j = i % db.NL
+        pkv.paged_kv_append(db.k[j], db.v[j], db.pt, app_bi, app_pos, app_k, app_v,
                             page_size=c.page_size)
         decode_only(i)
-
-    def decode_step_fused(i):
-        pkv.paged_decode_attn_append(d_q, d_rk, d_rv, d_k[i % NL], d_v[i % NL], d_pt, d_bi, d_kl,
-                                     page_size=c.page_size, scale=float(c.scale),
-                                     max_kv_len=max_kv, num_splits=S, flags=args.flags,
-                                     workspace=d_ws, out=d_out, lse=d_lse)
 
     decode_step = decode_step_separate if args.separate else decode_step_fused
 
@@ -225,7 +560,7 @@ def main():
 
     # ---------------- chunked prefill over a paged prefix (64 sequences), one pool set per layer
     chunked = None
-    if not args.no_chunked:
+    if not args.no_chunked and args.only is None:
         from workloads import make_chunked_prefill_case
         crng = np.random.default_rng(9305)
         cc = make_chunked_prefill_case(name="chunked", seed=9305,
@@ -248,60 +583,16 @@ def main():
 
         chunked = dict(case=cc, step=chunked_step, layers=NC)
 
-    flush_buf = torch.ones(1024 * 1024 * 1024 // 4, dtype=torch.float32, device=dev) \
-        if args.flush else None
-    flush_sink = torch.empty((), dtype=torch.float32, device=dev)
-
-    def timed(fn, n, replays=None):
-        """Device time (ms) of n steps fn(0..n-1).  With a list `replays`, the captured
-        graph is replayed 5 more times and each replay's time (ms) is appended to it."""
-        if args.flush:  # each call alone after a 1 GiB read (clean eviction)
-            total = 0.0
-            for i in range(n):
-                torch.sum(flush_buf, dim=0, out=flush_sink)
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                fn(i)
-                e1.record(stream)
-                e1.synchronize()
-                total += e0.elapsed_time(e1)
-            return total
-        if args.eager:
-            torch.cuda.synchronize()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for i in range(n):
-                fn(i)
-            e1.record(stream)
-            e1.synchronize()
-            return e0.elapsed_time(e1)
-        # The n steps are captured once into a HIP graph (as a serving loop
-        # captures its decode step) and replayed: the timed region holds the
-        # GPU work only, not Python's per-call launch cost.  All buffers are
-        # allocated before the capture; no memset is recorded.
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(n):
-                fn(i)
-        graph.replay()                      # first replay uploads the graph
+    # ---------------- profiling runs: one attention call type only
+    if args.only is not None:
+        fn = decode_only if args.only == "decode" else prefill["attn"]
+        for i in range(args.warmup):
+            fn(i)
         torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        graph.replay()
-        e1.record(stream)
-        e1.synchronize()
-        total = e0.elapsed_time(e1)
-        if replays is not None:
-            for _ in range(5):
-                e0.record(stream)
-                graph.replay()
-                e1.record(stream)
-                e1.synchronize()
-                replays.append(e0.elapsed_time(e1))
-        return total
+        ms = timer(fn, K) / K
+        print(json.dumps({"only": args.only, "avg_call_us": round(ms * 1e3, 3), "steps": K}),
+              flush=True)
+        return
 
     # ---------------- warmup
     for i in range(args.warmup):
@@ -311,32 +602,33 @@ def main():
         if chunked:
             chunked["step"](i)
     torch.cuda.synchronize()
+    progress("warmup done")
 
     # ---------------- timed steps
-    K = args.steps
     t0 = time.perf_counter()
-    dec_total = timed(decode_step, K)
-    pre_total = timed(prefill["step"], K) if prefill else 0.0
+    dec_total = timer(decode_step, K)
+    pre_total = timer(prefill["step"], K) if prefill else 0.0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     # the dominant kernels alone (roofline): decode attention, prefill attention
     dk_reps, pa_reps = [], []
-    dk_total = timed(decode_only, K, dk_reps)
-    alt_total = timed(decode_step_fused if args.separate else decode_step_separate, K)
-    pa_total = timed(prefill["attn"], K, pa_reps) if prefill else 0.0
-    palt_total = timed(prefill["alt"], K) if prefill else 0.0
-    ch_total = timed(chunked["step"], K) if chunked else 0.0
+    dk_total = timer(decode_only, K, dk_reps)
+    alt_total = timer(decode_step_fused if args.separate else decode_step_separate, K)
+    pa_total = timer(prefill["attn"], K, pa_reps) if prefill else 0.0
+    palt_total = timer(prefill["alt"], K) if prefill else 0.0
+    ch_total = timer(chunked["step"], K) if chunked else 0.0
     # warm, for context: every call reads the same cache (input set), which
     # then sits in the 256 MiB Infinity Cache; not an HBM figure
-    dw_total = timed(lambda i: decode_only(0), K)
-    pw_total = timed(lambda i: prefill["attn"](0), K) if prefill else 0.0
+    dw_total = timer(db.call(S, args.flags, rotate=False), K)
+    pw_total = timer(lambda i: prefill["attn"](0), K) if prefill else 0.0
+    progress("headline steps timed")
 
     dec_ms, dk_ms = dec_total / K, dk_total / K
     value = kv_bytes / (dec_ms * 1e-3) / 1e9
     achieved = kv_bytes / (dk_ms * 1e-3) / 1e9
     cache = ("flushed: 1 GiB read before each call" if args.flush else
-             f"cold: {NL} KV caches (one per layer) read round-robin, "
-             f"{(NL - 1) * kv_bytes / 1e9:.2f} GB of other KV between reuses")
+             f"cold: {db.NL} KV caches (one per layer) read round-robin, "
+             f"{(db.NL - 1) * kv_bytes / 1e9:.2f} GB of other KV between reuses")
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -360,8 +652,7 @@ def main():
             "decode_step": ("paged_kv_append + paged_decode_attn" if args.separate else
                             "paged_decode_attn_append (append and decode fused in one launch)"),
             ("fused_step_ms" if args.separate else "separate_step_ms"): round(alt_total / K, 5),
-            "schedule": (f"balanced: {W} workgroups per KV head" if balanced else
-                         f"per-row: {S} split(s) per row"),
+            "schedule": sched,
             "launch": "eager stream launches" if (args.eager or args.flush) else
                       f"one HIP graph of the {K} timed steps, replayed once",
             "flags": int(args.flags),
@@ -370,7 +661,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": decode_kernels(S, W) + " (one paged_decode_attn call)",
+            "kernel": decode_kernels(S_eff, W) + " (one paged_decode_attn call)",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -416,6 +707,10 @@ def main():
                 "compulsory_bytes": int(p_bytes),
                 "hbm_achieved_gbs": round(p_bytes / (pa_ms * 1e-3) / 1e9, 2),
                 "hbm_frac": round(p_bytes / (pa_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                # the binding roof at this intensity: min(matrix peak, intensity x HBM peak)
+                "intensity_flop_per_byte": round(flops / p_bytes, 1),
+                "frac_of_intensity_roof": round(
+                    tflops / min(BF16_PEAK_TFLOPS, flops / p_bytes * HBM_PEAK_GBS / 1e3), 4),
                 "replays_us": ({"median": round(float(np.median(pa_reps)) / K * 1e3, 3),
                                 "best": round(min(pa_reps) / K * 1e3, 3), "n": len(pa_reps)}
                                if pa_reps else None),
@@ -440,32 +735,84 @@ def main():
             "prefix_kv_bytes": kv_prefix,
             "cache": f"cold: {chunked['layers']} pool sets read round-robin",
         }
+
+    # ---------------- every named workload on its own
+    cases = {3: c}
+    if not args.no_configs:
+        cfgs = {}
+        # B=64 bucket: the contiguous-page path against the page-table walk, same layout
+        ab = {}
+        for name, fl in (("detect (default)", 0), ("walk (PKV_F_NO_CONTIG_DETECT)",
+                                                   pkv.PKV_F_NO_CONTIG_DETECT),
+                         ("assume (PKV_F_ASSUME_CONTIGUOUS)", pkv.PKV_F_ASSUME_CONTIGUOUS)):
+            r, _ = time_decode(timer, db, K, S, args.flags | fl, warm=False, replays=True)
+            ab[name] = r
+        cfgs["3"] = {"workload": out["config"]["workload"] + " (decode call alone)",
+                     "kv_bytes": int(kv_bytes), "schedule": sched,
+                     "contiguous_path": ab,
+                     "note": "same sequential pages, same schedule; cold rotating caches"}
+        progress("config 3 paths timed")
+        # tiny decode: launch-bound, context only
+        c1 = cases[1] = make_case(1, fill="zero")
+        d1 = DecodeBench(torch, pkv, c1, dev, layers=2)
+        r1 = {}
+        for S1, fl1, nm in ((0, 0, "auto"), (2, 0, "split 2"), (0, pkv.PKV_F_BALANCED, "balanced")):
+            rr, _ = time_decode(timer, d1, K, S1, fl1)
+            r1[nm + " (" + plan_name(pkv, c1, S1, fl1, d1.max_kv)[0] + ")"] = rr
+        cfgs["1"] = {"workload": "tiny decode B=3 (slot 0 padding), H_q=4 H_kv=2 D=64 "
+                                 "page_size=16, 37 and 70 keys", "kv_bytes": int(d1.kv_bytes),
+                     "schedules": r1, "note": "launch-bound; context only"}
+        d1.free()
+        # B=8 Qwen3-4B decode + append
+        c2 = cases[2] = make_case(2, fill="zero")
+        d2 = DecodeBench(torch, pkv, c2, dev)
+        r2 = {}
+        for S2, fl2, nm in ((0, 0, "auto"), (1, 0, "single pass"),
+                            (0, pkv.PKV_F_BALANCED, "balanced")):
+            rr, _ = time_decode(timer, d2, K, S2, fl2, replays=(nm == "auto"))
+            r2[nm + " (" + plan_name(pkv, c2, S2, fl2, d2.max_kv)[0] + ")"] = rr
+        app_ms = timer(d2.fused(0, 0), K) / K
+        cfgs["2"] = {"workload": "Qwen3-4B decode B=8, H_q=32 H_kv=8 D=128 page_size=128, "
+                                 "contexts U[256,1536], shuffled pages",
+                     "kv_bytes": int(d2.kv_bytes), "layers": d2.NL, "schedules": r2,
+                     "fused_append_step_us": round(app_ms * 1e3, 3)}
+        d2.free()
+        progress("config 2 timed")
+        # B=256, 4096-page pool: automatic plan, split-K + merge, balanced
+        c4 = cases[4] = make_case(4, fill="zero")
+        d4 = DecodeBench(torch, pkv, c4, dev)
+        r4 = {}
+        for S4, fl4, nm in ((0, 0, "auto"), (2, 0, "split-K 2 + merge"),
+                            (4, 0, "split-K 4 + merge"), (0, pkv.PKV_F_BALANCED, "balanced")):
+            rr, _ = time_decode(timer, d4, max(4, K // 4), S4, fl4, replays=(nm == "auto"))
+            r4[nm + " (" + plan_name(pkv, c4, S4, fl4, d4.max_kv)[0] + ")"] = rr
+        cfgs["4"] = {"workload": "large-batch decode B=256, H_q=32 H_kv=8 D=128 page_size=128, "
+                                 "contexts U[1024,2048], 4096-page pool, shuffled pages",
+                     "kv_bytes": int(d4.kv_bytes), "layers": d4.NL, "schedules": r4}
+        d4.free()
+        progress("config 4 timed")
+        if prefill:
+            cfgs["5"] = {"workload": out["prefill"]["workload"],
+                         "see": "prefill (attention call) and prefill.roofline"}
+        out["configs"] = cfgs
+
+    if not args.no_ceilings:
+        out["ceilings"] = ceilings(torch, timer, dev, db, K)
+        progress("ceilings measured")
+
     if args.cpu_seconds > 0:
-        out["cpu_baseline"] = cpu_baseline(c, kv_bytes, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_decode_baseline(c, args.cpu_seconds, single=False)
+        out["cpu_baseline"]["cpu_model"] = cpu_model()
+        if not args.no_configs:
+            per = {}
+            for k in (1, 2, 3, 4):
+                per[str(k)] = cpu_decode_baseline(cases[k], args.cpu_seconds)
+            if prefill:
+                per["5"] = cpu_prefill_baseline(prefill["case"], args.cpu_seconds)
+            out["cpu_baselines"] = {"cpu_model": cpu_model(), "nproc": os.cpu_count(),
+                                    "per_config": per}
+        progress("oracle timed")
     print(json.dumps(out), flush=True)
-
-
-def cpu_baseline(c, kv_bytes, budget_s):
-    """The float64 oracle timed on the host cores over the same decode workload."""
-    import oracle
-
-    B = c.B
-    lo = np.zeros(B, np.int32)
-    reps, t_total = 0, 0.0
-    while t_total < budget_s or reps == 0:
-        t0 = time.perf_counter()
-        oracle.decode(c.q, c.k_pool, c.v_pool, c.num_pages, c.page_size, c.page_table,
-                      c.batch_idx, lo, c.kv_len, c.scale)
-        t_total += time.perf_counter() - t0
-        reps += 1
-    return {
-        "value": round(kv_bytes * reps / t_total / 1e9, 4),
-        "unit": "GB/s",
-        "cores": oracle.num_threads(),
-        "kind": "oracle",
-        "sample": f"the full B=64 decode step (50 live rows, {kv_bytes / 1e6:.1f} MB of KV), "
-                  f"repeated {reps}x in {t_total:.1f} s",
-    }
 
 
 if __name__ == "__main__":

@@ -1,4 +1,5 @@
-"""Build libpkv.so (every HIP source under csrc/) for gfx950 with hipcc.
+"""Build libpkv.so (every HIP source under csrc/) for gfx950 with hipcc, and the
+benchmark's probe library measure/libpkvceil.so.
 
 Run as `python -m paged_kv_attention_23_amd.build` or through
 __graft_entry__.build().  The library lands next to this file.
@@ -35,6 +36,22 @@ def _compile(src: str, obj: str, save_temps_dir: str | None) -> None:
             print(line, file=sys.stderr)
 
 
+MEASURE_SRC = os.path.join(HERE, "measure", "ceilings.hip")
+MEASURE_LIB = os.path.join(HERE, "measure", "libpkvceil.so")
+
+
+def build_measure() -> str:
+    """The benchmark's reachable-rate probes (plain read, decode-shaped streaming,
+    dense matrix loop) as their own small library, outside the attention ABI."""
+    tmp = MEASURE_LIB + ".tmp"
+    p = subprocess.run(["hipcc", *HIP_FLAGS, "-shared", MEASURE_SRC, "-o", tmp],
+                       capture_output=True, text=True)
+    if p.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {MEASURE_SRC}:\n{p.stderr}")
+    os.replace(tmp, MEASURE_LIB)
+    return MEASURE_LIB
+
+
 def build(save_temps_dir: str | None = None) -> str:
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     objdir = os.path.join(HERE, "_build")
@@ -51,6 +68,7 @@ def build(save_temps_dir: str | None = None) -> str:
     if p.returncode != 0:
         raise RuntimeError(f"link failed:\n{p.stderr}")
     os.replace(tmp, LIB)
+    build_measure()
     return LIB
 
 

@@ -1,0 +1,144 @@
+// Reachable-rate probes that the benchmark reports beside the attention
+// kernels' figures (libpkvceil.so, loaded by bench.py only; not part of the
+// attention library's ABI).  They compute nothing useful: each one moves
+// bytes or issues matrix instructions at the fastest rate a plain kernel of
+// its shape reaches on this GPU, and keeps its results alive with a
+// data-dependent store that never fires for the inputs the benchmark uses.
+//
+//   ceil_stream_read   one grid-strided front of non-temporal 16-byte loads
+//                      over a buffer (the plain HBM read ceiling)
+//   ceil_stream_units  the decode launch shape with the arithmetic taken
+//                      out: one workgroup of 4 waves per (row, KV head) unit,
+//                      each reading its unit's K and V rows (contiguous runs
+//                      given by the caller) in 32-key tiles dealt to waves in
+//                      turn, one tile in flight per wave
+//   ceil_mfma          back-to-back 16x16x32 bf16 matrix instructions,
+//                      16 independent accumulators per wave, two waves per
+//                      SIMD (the dense bf16 rate of the instruction the
+//                      attention kernels use)
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 ld_nt(const u32x4 *p) { return __builtin_nontemporal_load(p); }
+
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4 *__restrict__ p, uint64_t n,
+                                                          uint32_t key, uint32_t *sink) {
+  const uint64_t stride = (uint64_t)gridDim.x * 256u;
+  uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    const u32x4 a = ld_nt(p + i), b = ld_nt(p + i + stride), c = ld_nt(p + i + 2 * stride),
+                d = ld_nt(p + i + 3 * stride);
+    acc ^= a ^ b ^ c ^ d;
+  }
+  for (; i < n; i += stride) acc ^= ld_nt(p + i);
+  const uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  if (x == key) sink[blockIdx.x & 1023u] = x;
+}
+
+// units[2*u] = first pool row of unit u's keys in its KV head plane (K and V
+// use the same rows), units[2*u+1] = its number of keys (0: padding, the
+// workgroup exits).  Unit u belongs to KV head u % H_kv.
+__global__ __launch_bounds__(256) void stream_units_kernel(const char *__restrict__ kpool,
+                                                           const char *__restrict__ vpool,
+                                                           uint64_t plane_bytes, int H_kv,
+                                                           const int32_t *__restrict__ units,
+                                                           uint32_t key, uint32_t *sink) {
+  const int u = blockIdx.x;
+  const int row0 = units[2 * u], n = units[2 * u + 1];
+  if (n <= 0) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t head = (uint64_t)(u % H_kv) * plane_bytes;
+  const char *kb = kpool + head + (uint64_t)row0 * 256u;
+  const char *vb = vpool + head + (uint64_t)row0 * 256u;
+  // A 32-key tile of one tensor is 8 KB: 8 loads of 16 bytes per lane; lane l
+  // reads key row 4*i + l/16, column l%16 in load i.
+  const int ntiles = (n + 31) / 32;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  u32x4 kr[8], vr[8];
+  auto issue = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      int key_row = 32 * t + 4 * i + (lane >> 4);
+      key_row = key_row < n ? key_row : n - 1;
+      const uint32_t off = (uint32_t)key_row * 256u + (uint32_t)(lane & 15) * 16u;
+      kr[i] = ld_nt(reinterpret_cast<const u32x4 *>(kb + off));
+      vr[i] = ld_nt(reinterpret_cast<const u32x4 *>(vb + off));
+    }
+  };
+  int t = wave;
+  if (t < ntiles) issue(t);
+  while (t < ntiles) {
+    u32x4 k2[8], v2[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      k2[i] = kr[i];
+      v2[i] = vr[i];
+    }
+    const int tn = t + 4;
+    if (tn < ntiles) issue(tn);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc ^= k2[i] ^ v2[i];
+    t = tn;
+  }
+  const uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  if (x == key) sink[u & 1023] = x;
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void mfma_kernel(int iters, float key, float *sink) {
+  const float s = (float)(threadIdx.x & 7) * 0.001f;
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(s + 0.01f * i);
+    b[i] = (__bf16)(0.5f - s);
+  }
+  f32x4 acc[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+  }
+  float t = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) t += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+  if (t == key) sink[blockIdx.x & 1023] = t;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Grids are the caller's; every kernel is bounded by its arguments.
+int ceil_stream_read(const void *buf, uint64_t bytes, int grid, uint32_t *sink, void *stream) {
+  if (!buf || !sink || grid <= 0 || (bytes & 15u)) return -1;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream,
+                     (const u32x4 *)buf, bytes / 16u, 0x9e3779b9u, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+int ceil_stream_units(const void *kpool, const void *vpool, uint64_t plane_bytes, int H_kv,
+                      const int32_t *units, int num_units, uint32_t *sink, void *stream) {
+  if (!kpool || !vpool || !units || !sink || H_kv <= 0 || num_units <= 0) return -1;
+  hipLaunchKernelGGL(stream_units_kernel, dim3(num_units), dim3(256), 0, (hipStream_t)stream,
+                     (const char *)kpool, (const char *)vpool, plane_bytes, H_kv, units,
+                     0x9e3779b9u, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+int ceil_mfma(int grid, int iters, float *sink, void *stream) {
+  if (!sink || grid <= 0 || iters <= 0) return -1;
+  hipLaunchKernelGGL(mfma_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, iters, -1.0f,
+                     sink);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+}  // extern "C"
