@@ -3,7 +3,8 @@
  *
  * C ABI of libpkv.so.  Every tensor argument is a plain DEVICE pointer owned by
  * the caller; the library allocates no memory, keeps no state between calls
- * (apart from a cached device-property query), never synchronises, and only
+ * (apart from a cached device-property query, and the fixed scratch array of
+ * paged_decode_attn_noalloc), never synchronises, and only
  * enqueues work on the HIP stream passed in `stream` (a hipStream_t; NULL is
  * the default stream).  bf16 tensors are raw bfloat16 bit patterns, densely
  * packed (row-major, innermost dimension contiguous), 16-byte aligned.
@@ -167,6 +168,34 @@ int paged_decode_attn(const void *q, const void *k_pool, const void *v_pool, int
                       int32_t num_q_heads, float scale, int32_t max_kv_len, int32_t num_splits,
                       uint32_t flags, void *workspace, size_t workspace_bytes, void *out,
                       float *lse, void *stream);
+
+/*
+ * paged_decode_attn_noalloc - paged_decode_attn for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).
+ *
+ * Arguments, schedule choice and results are those of paged_decode_attn with
+ * the same num_splits and flags; there is no workspace argument.  The split
+ * partials and descriptors go to a fixed scratch array inside the library,
+ * 16 MiB per GPU (held by each GPU the library runs on until the process
+ * ends).  A plan whose paged_decode_workspace_size exceeds 16 MiB is rejected
+ * with PKV_E_WORKSPACE before anything is launched; every automatic plan on
+ * head_dim <= 128 with at most 16 query heads per KV head fits.  The call
+ * allocates nothing: the scratch address is looked up once per device
+ * (hipGetSymbolAddress, with that device current) on the first call on it
+ * whose plan writes partials; a failed lookup returns PKV_E_HIP.
+ * Nothing in the scratch needs clearing between calls (every partial a call
+ * reads is written by that call).  All calls on one GPU share its scratch:
+ * calls that overlap in time on one GPU (different streams, or host threads)
+ * race and give undefined results; serialise them on one stream.
+ */
+int paged_decode_attn_noalloc(const void *q, const void *k_pool, const void *v_pool,
+                              int32_t num_pages, int32_t page_size, int32_t num_kv_heads,
+                              int32_t head_dim, const int32_t *page_table, int32_t num_slots,
+                              int32_t max_blocks, const int32_t *batch_idx, const int32_t *kv_len,
+                              int32_t batch, int32_t num_q_heads, float scale, int32_t max_kv_len,
+                              int32_t num_splits, uint32_t flags, void *out, float *lse,
+                              void *stream);
 
 /*
  * paged_decode_attn_append - paged_kv_append of each row's new token

@@ -7,6 +7,9 @@ libpkv.so (include/pkv.h):
   paged_decode_attn    one query token per row over its paged keys
                        (single pass, per-row or balanced split-K + merge,
                        contiguous-page fast path)
+  paged_decode_attn_noalloc
+                       paged_decode_attn for callers that cannot allocate:
+                       split partials in a fixed per-GPU scratch array
   paged_decode_attn_append
                        the two above fused: each row's new token is
                        attended from registers and written into its page
@@ -34,6 +37,7 @@ from ._binding import (  # noqa: F401
     packed_prefill_attn_append,
     paged_decode_attn,
     paged_decode_attn_append,
+    paged_decode_attn_noalloc,
     paged_decode_balanced_parts,
     paged_decode_num_splits,
     paged_decode_workspace_size,

@@ -67,6 +67,10 @@ def load_library(path: str = LIB_PATH):
                                     _I32, _I32, ctypes.c_float, _I32, _I32, ctypes.c_uint32, _P,
                                     ctypes.c_size_t, _P, _P, _P]
     L.paged_decode_attn.restype = ctypes.c_int
+    L.paged_decode_attn_noalloc.argtypes = [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _I32, _I32,
+                                            _P, _P, _I32, _I32, ctypes.c_float, _I32, _I32,
+                                            ctypes.c_uint32, _P, _P, _P]
+    L.paged_decode_attn_noalloc.restype = ctypes.c_int
     L.paged_decode_attn_append.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _I32,
                                            _I32, _P, _P, _I32, _I32, ctypes.c_float, _I32, _I32,
                                            ctypes.c_uint32, _P, ctypes.c_size_t, _P, _P, _P]
@@ -226,6 +230,30 @@ def paged_decode_attn(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tenso
                              int(max_kv_len), int(num_splits), int(flags), ws_ptr, ws_bytes,
                              p["out"], p["lse"], _stream(stream))
     _check(rc, "paged_decode_attn")
+    return out, lse
+
+
+def paged_decode_attn_noalloc(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                              page_table: torch.Tensor, batch_idx: torch.Tensor,
+                              kv_len: torch.Tensor, page_size: int, scale: float,
+                              out: torch.Tensor, lse: torch.Tensor, max_kv_len: int = 0,
+                              num_splits: int = 0, flags: int = 0,
+                              stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """paged_decode_attn without a workspace: split partials go to the library's fixed
+    per-GPU scratch, so neither this call nor the library allocates anything.  The
+    caller passes out and lse.  Calls overlapping on one GPU share that scratch."""
+    if out is None or lse is None:
+        raise ValueError("paged_decode_attn_noalloc writes into caller buffers: pass out and lse")
+    L = load_library()
+    p, g, _, _, out, lse = _decode_args(q, k_pool, v_pool, page_table, batch_idx, kv_len,
+                                        page_size, num_splits, flags, None, out, lse,
+                                        alloc_workspace=False)
+    rc = L.paged_decode_attn_noalloc(p["q"], p["k_pool"], p["v_pool"], g["num_pages"], page_size,
+                                     g["H_kv"], g["D"], p["page_table"], g["num_slots"],
+                                     g["max_blocks"], p["batch_idx"], p["kv_len"], g["B"],
+                                     g["H_q"], float(scale), int(max_kv_len), int(num_splits),
+                                     int(flags), p["out"], p["lse"], _stream(stream))
+    _check(rc, "paged_decode_attn_noalloc")
     return out, lse
 
 

@@ -6,6 +6,7 @@
 #include <stdio.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/pkv.h"
 #include "pkv_internal.h"
@@ -256,6 +257,33 @@ int32_t paged_decode_balanced_parts(int32_t batch, int32_t num_kv_heads, int32_t
   return balanced_parts(batch, num_kv_heads, max_kv_len > 0 ? max_kv_len : 1, device_cus());
 }
 
+// Scratch of paged_decode_attn_noalloc: the split partials and descriptors
+// live in this fixed device array instead of a caller workspace.  Each GPU
+// the library runs on holds its own copy until the process ends.  In host
+// code the array's name is only a stand-in, so its device address is taken
+// once per device with hipGetSymbolAddress and used everywhere instead.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+static int scratch_address(void **out) {
+  static std::mutex mu;
+  static void *addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PKV_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(PKV_E_SHAPE, "device %d is beyond the scratch table", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(PKV_E_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return PKV_OK;
+}
+
 static int decode_common(const char *who, const void *q, const void *k_new, const void *v_new,
                          const void *k_pool, const void *v_pool, bool fused, int32_t num_pages,
                          int32_t page_size, int32_t num_kv_heads, int32_t head_dim,
@@ -263,7 +291,7 @@ static int decode_common(const char *who, const void *q, const void *k_new, cons
                          const int32_t *batch_idx, const int32_t *kv_len, int32_t batch,
                          int32_t num_q_heads, float scale, int32_t max_kv_len, int32_t num_splits,
                          uint32_t flags, void *workspace, size_t workspace_bytes, void *out,
-                         float *lse, void *stream) {
+                         float *lse, void *stream, bool noalloc = false) {
   if (batch < 0) return fail(PKV_E_SHAPE, "batch must be >= 0 (got %d)", batch);
   int rc = check_pool(num_pages, page_size, num_kv_heads, head_dim, num_slots, max_blocks);
   if (rc) return rc;
@@ -316,6 +344,15 @@ static int decode_common(const char *who, const void *q, const void *k_new, cons
   if (S > 1) {
     const size_t need = paged_decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim,
                                                     balanced ? 0 : S, flags);
+    if (noalloc) {  // partials in the fixed scratch instead of a caller workspace
+      if (need > kNoAllocScratchBytes)
+        return fail(PKV_E_WORKSPACE,
+                    "%s: this plan needs %zu bytes of scratch, above the fixed maximum of %zu",
+                    who, need, kNoAllocScratchBytes);
+      int rc2 = scratch_address(&workspace);
+      if (rc2) return rc2;
+      workspace_bytes = kNoAllocScratchBytes;
+    }
     if (!workspace || workspace_bytes < need)
       return fail(PKV_E_WORKSPACE, "%s: %s needs %zu workspace bytes (got %zu%s)", who,
                   balanced ? "the balanced schedule" : "this split count", need, workspace_bytes,
@@ -379,6 +416,19 @@ int paged_decode_attn(const void *q, const void *k_pool, const void *v_pool, int
                        page_size, num_kv_heads, head_dim, page_table, num_slots, max_blocks,
                        batch_idx, kv_len, batch, num_q_heads, scale, max_kv_len, num_splits, flags,
                        workspace, workspace_bytes, out, lse, stream);
+}
+
+int paged_decode_attn_noalloc(const void *q, const void *k_pool, const void *v_pool,
+                              int32_t num_pages, int32_t page_size, int32_t num_kv_heads,
+                              int32_t head_dim, const int32_t *page_table, int32_t num_slots,
+                              int32_t max_blocks, const int32_t *batch_idx, const int32_t *kv_len,
+                              int32_t batch, int32_t num_q_heads, float scale, int32_t max_kv_len,
+                              int32_t num_splits, uint32_t flags, void *out, float *lse,
+                              void *stream) {
+  return decode_common("paged_decode_attn_noalloc", q, nullptr, nullptr, k_pool, v_pool, false,
+                       num_pages, page_size, num_kv_heads, head_dim, page_table, num_slots,
+                       max_blocks, batch_idx, kv_len, batch, num_q_heads, scale, max_kv_len,
+                       num_splits, flags, nullptr, 0, out, lse, stream, true);
 }
 
 int paged_decode_attn_append(const void *q, const void *k_new, const void *v_new, void *k_pool,

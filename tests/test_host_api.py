@@ -221,3 +221,27 @@ def test_graph_buckets():
     assert default_buckets(64) == [1, 2, 4, 8, 16, 32, 48, 64]
     assert default_buckets(50) == [1, 2, 4, 8, 16, 32, 48, 50]
     assert default_buckets(3) == [1, 2, 3]
+
+
+def test_noalloc_host_checks(lib):
+    """paged_decode_attn_noalloc: an empty batch is a no-op, a plan whose partials exceed
+    the fixed scratch is refused before any HIP call, and bad shapes fail as in
+    paged_decode_attn."""
+    f = lib.paged_decode_attn_noalloc
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, num_pages=8, page_size=16, H_kv=8, D=128, pt=FAKE,
+                 num_slots=3, max_blocks=4, bi=FAKE, kl=FAKE, batch=2, H_q=32, scale=0.125,
+                 max_kv_len=64, splits=1, flags=0, out=FAKE, lse=FAKE, stream=0)
+        a.update(kw)
+        return f(a["q"], a["k"], a["v"], a["num_pages"], a["page_size"], a["H_kv"], a["D"],
+                 a["pt"], a["num_slots"], a["max_blocks"], a["bi"], a["kl"], a["batch"], a["H_q"],
+                 a["scale"], a["max_kv_len"], a["splits"], a["flags"], a["out"], a["lse"],
+                 a["stream"])
+
+    assert call(batch=0, q=0, k=0, v=0, pt=0, bi=0, kl=0, out=0, lse=0) == 0
+    rc = call(batch=4096, splits=64)  # 64 * 4096 * 32 * 129 * 4 bytes of partials
+    assert rc == B._C["PKV_E_WORKSPACE"], (rc, B.last_error())
+    assert "scratch" in B.last_error() and "paged_decode_attn_noalloc" in B.last_error()
+    assert call(D=96) == -2
+    assert call(splits=65) == B._C["PKV_E_SPLITS"]
