@@ -276,7 +276,7 @@ class DecodeBench:
 
 
 def plan_name(pkv, c, S, flags, max_kv):
-    if flags & pkv.PKV_F_BALANCED or (S == 0 and max_kv > 2048):
+    if flags & pkv.PKV_F_BALANCED or (S == 0 and pkv.paged_decode_auto_balanced(c.B, c.H_kv, max_kv)):
         W = pkv.paged_decode_balanced_parts(c.B, c.H_kv, max_kv)
         return f"balanced: {W} workgroups per KV head", 1, W
     s = S or pkv.paged_decode_num_splits(c.B, c.H_kv, max_kv)

@@ -93,10 +93,21 @@ size_t paged_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t n
 /*
  * paged_decode_num_splits - the per-row split count paged_decode_attn
  * chooses for num_splits == 0 (without PKV_F_BALANCED) on the current device
- * when max_kv_len is at most 2048 (above it the automatic choice is the
- * balanced schedule).  Host function.
+ * when that automatic choice is the per-row schedule (see
+ * paged_decode_auto_balanced).  Host function.
  */
 int32_t paged_decode_num_splits(int32_t batch, int32_t num_kv_heads, int32_t max_kv_len);
+
+/*
+ * paged_decode_auto_balanced - 1 when paged_decode_attn with num_splits == 0
+ * (and no PKV_F_BALANCED) takes the balanced schedule on the current device
+ * for this batch and key bound max_kv_len: a key bound above 2048, or at
+ * least 4 (row, KV head) units per compute unit; 0 when it takes the per-row
+ * schedule, and for non-positive arguments.  A scheduling choice of this
+ * library: the decode block mask of the qwen3_flex_inference.py page fixes
+ * what is attended, not how the work is split.  Host function.
+ */
+int32_t paged_decode_auto_balanced(int32_t batch, int32_t num_kv_heads, int32_t max_kv_len);
 
 /*
  * paged_decode_balanced_parts - the number W of workgroups per KV head that
@@ -132,10 +143,12 @@ int32_t paged_decode_balanced_parts(int32_t batch, int32_t num_kv_heads, int32_t
  *                loose bound costs speed, never correctness
  *   num_splits   split-K (flash-decoding; the pages leave the decode kernel's
  *                work split open, so the schedules are the library's own):
- *                0 = automatic: when the key bound (max_kv_len, else
- *                    max_blocks*page_size) is at most 2048, the per-row
- *                    schedule with paged_decode_num_splits splits; above it
- *                    the balanced schedule below (long or skewed contexts),
+ *                0 = automatic: the balanced schedule below when the key
+ *                    bound (max_kv_len, else max_blocks*page_size) is above
+ *                    2048 (long or skewed contexts) or when batch *
+ *                    num_kv_heads is at least 4 per compute unit (large
+ *                    batches); otherwise the per-row schedule with
+ *                    paged_decode_num_splits splits,
  *                1 = one workgroup per (row, KV head), single pass,
  *                2..PKV_MAX_SPLITS = each row's keys in that many equal parts,
  *                    merged by log-sum-exp in a second kernel.

@@ -38,6 +38,7 @@ from ._binding import (  # noqa: F401
     paged_decode_attn,
     paged_decode_attn_append,
     paged_decode_attn_noalloc,
+    paged_decode_auto_balanced,
     paged_decode_balanced_parts,
     paged_decode_num_splits,
     paged_decode_workspace_size,

@@ -63,6 +63,8 @@ def load_library(path: str = LIB_PATH):
     L.paged_decode_num_splits.restype = _I32
     L.paged_decode_balanced_parts.argtypes = [_I32, _I32, _I32]
     L.paged_decode_balanced_parts.restype = _I32
+    L.paged_decode_auto_balanced.argtypes = [_I32, _I32, _I32]
+    L.paged_decode_auto_balanced.restype = _I32
     L.paged_decode_attn.argtypes = [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _I32, _I32, _P, _P,
                                     _I32, _I32, ctypes.c_float, _I32, _I32, ctypes.c_uint32, _P,
                                     ctypes.c_size_t, _P, _P, _P]
@@ -175,6 +177,10 @@ def paged_decode_balanced_parts(batch: int, num_kv_heads: int, max_kv_len: int) 
     return int(load_library().paged_decode_balanced_parts(batch, num_kv_heads, max_kv_len))
 
 
+def paged_decode_auto_balanced(batch: int, num_kv_heads: int, max_kv_len: int) -> bool:
+    return bool(load_library().paged_decode_auto_balanced(batch, num_kv_heads, max_kv_len))
+
+
 def _decode_args(q, k_pool, v_pool, page_table, batch_idx, kv_len, page_size, num_splits, flags,
                  workspace, out, lse, alloc_workspace=True):
     """Shapes, pointers and output buffers shared by the decode wrappers."""
@@ -214,9 +220,10 @@ def paged_decode_attn(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tenso
                       stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Decode attention; returns (out bf16 [B, H_q, D], lse fp32 [B, H_q]).
 
-    num_splits = 0 chooses automatically (per-row splits up to a key bound of
-    2048, the balanced schedule above it), 1 is a single pass, >1 per-row
-    splits; flags |= PKV_F_BALANCED (with num_splits = 0) forces the balanced
+    num_splits = 0 chooses automatically (the balanced schedule for a key
+    bound above 2048 or at least 4 (row, KV head) units per compute unit,
+    per-row splits otherwise: paged_decode_auto_balanced), 1 is a single
+    pass, >1 per-row splits; flags |= PKV_F_BALANCED (with num_splits = 0) forces the balanced
     schedule.  The workspace (uint8 tensor) is allocated
     here when not given and the schedule needs one.
     """

@@ -86,6 +86,7 @@ def _decode(lib, **kw):
     (dict(splits=2, flags=4), -5, "num_splits"),
     (dict(splits=0, flags=4), -4, "workspace"),
     (dict(splits=0, max_kv_len=4096, max_blocks=300), -4, "balanced"),   # automatic, long context
+    (dict(splits=0, batch=128, H_kv=8, H_q=32), -4, "balanced"),        # automatic, 4 units per CU
     (dict(splits=2, ws=FAKE, ws_bytes=100), -4, "workspace"),
     (dict(splits=2, ws=FAKE + 4, ws_bytes=1 << 20), -3, "workspace"),
 ])
