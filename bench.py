@@ -363,6 +363,8 @@ def load_ceil():
     L.ceil_stream_units.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int,
                                     ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     L.ceil_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    P, I, U = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint32
+    L.ceil_paged_units.argtypes = [P, P, ctypes.c_uint64, U, I, P, I, I, I, I, P, P, I, P, P]
     return L
 
 
@@ -433,6 +435,26 @@ def ceilings(torch, timer, dev, db3, K):
                 "frac_of_hbm_peak": round(db3.kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "note": "the B=64 decode's launch shape and bytes with no arithmetic: "
                         f"{c.B * c.H_kv} workgroups of 4 waves (one per row and KV head), cold"}
+        # the same launch shape reaching its keys the way paged decode does: slot and length,
+        # then the page-id window, then K/V through the page ids (the dependent-load chain
+        # without any arithmetic)
+        if c.max_blocks <= 64 and c.D == 128:
+            plane_bytes = c.num_pages * c.page_size * c.D * 2
+            shift = int(c.page_size).bit_length() - 1
+
+            def fp(i):
+                j = i % db3.NL
+                assert L.ceil_paged_units(db3.k[j].data_ptr(), db3.v[j].data_ptr(), plane_bytes,
+                                          c.D * 2, c.H_kv, db3.pt.data_ptr(), c.max_blocks, shift,
+                                          c.num_pages, c.num_slots, db3.bi.data_ptr(),
+                                          db3.kl.data_ptr(), c.B, sink.data_ptr(), st()) == 0
+            ms = timer(fp, K) / K
+            out["decode_shape_paged"] = {
+                "us": round(ms * 1e3, 3), "bytes": int(db3.kv_bytes),
+                "gbs": round(db3.kv_bytes / (ms * 1e-3) / 1e9, 1),
+                "frac_of_hbm_peak": round(db3.kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "note": "decode_shape_stream with the paged lookups: batch_idx and kv_len, one "
+                        "page-id window per unit, K/V rows through the page ids; no arithmetic"}
         fsink = torch.zeros(1024, dtype=torch.float32, device=dev)
         iters, grid = 4000, 2 * cus
 

@@ -8,18 +8,22 @@
 //  * One workgroup of 4 waves owns a (row, KV head, split) unit and reads each
 //    K/V row of its key range exactly once, serving all G query heads of that
 //    KV head.  Waves interleave over 32-key tiles of the range.
-//  * Scores: S^T[key][head] = K Q^T on the 16x16x32 bf16 matrix core, K
-//    loaded straight from HBM into the A-operand layout (lane = key row,
-//    16 contiguous bytes), Q held in B-operand registers for the whole unit
-//    (heads past G are zero columns).
+//  * Scores: S^T[key][head] = K Q^T on the 16x16x32 bf16 matrix core, Q
+//    held in B-operand registers for the whole unit (heads past G are zero
+//    columns).  K and V rows are loaded whole (each load instruction reads
+//    four complete rows) and staged in per-wave LDS tiles: reading K straight
+//    into the A-operand layout (16 rows x 64 bytes per instruction) asks the
+//    memory system for every cache line twice, which costs more than the
+//    LDS round trip.
 //  * Online softmax in base 2 in fp32 registers: each lane owns one head and
 //    eight keys of the tile.  Weights are taken against a lazily moved
 //    reference max; only a tile that exceeds it by the lazy threshold pays
 //    for the two cross-row shuffles of the tile max and the rescale.
 //  * O^T[d][head] += V^T P^T on the matrix core.  The score layout already is
-//    the B operand P^T (key order permuted consistently); V^T comes from a
-//    per-wave LDS tile through gfx950's transposing LDS reads, its key rows
-//    padded so those reads hit distinct banks.
+//    the B operand P^T (key order permuted consistently); V^T comes from the
+//    per-wave V tile through gfx950's transposing LDS reads.  Key rows in
+//    both tiles are padded by 16 bytes, so the row writes, the K operand
+//    reads and the transposing V reads all hit distinct banks.
 //  * The contiguous fast path (flex_vs_vllm.md page, option table: blocks
 //    are contiguous) replaces per-block page-table lookups with one linear
 //    row base when a unit's pages are consecutive ids.
@@ -39,16 +43,17 @@ constexpr float kDecLazy = 8.f;  // lazy-rescale threshold, log2 units
 
 template <int D>
 struct DecGeom {
-  static constexpr int kRowStride = 2 * D + 16;  // bytes per key row in a wave's V tile
-  static constexpr int kVBytes = kTileKeys * kRowStride;  // one wave's V tile
+  static constexpr int kRowStride = 2 * D + 16;  // bytes per key row in a wave's K or V tile
+  static constexpr int kVBytes = kTileKeys * kRowStride;  // one wave's K (or V) tile
   static constexpr int kDChunks = D / 32;    // QK steps over head_dim
   static constexpr int kDBlocks = D / 16;    // PV output blocks over head_dim
   static constexpr int kVLoads = D / 16;     // 16-byte V loads per lane per tile
   static constexpr int kLanesPerRow = D / 8; // lanes covering one key row in a V load
   static constexpr int kKeysPerLoad = kWave / kLanesPerRow;
   static constexpr int kMergeFloats = kDecWaves * 16 * D + kDecWaves * 16 * 2;
-  static constexpr int kSmemBytes = (kDecWaves * kVBytes > kMergeFloats * 4) ? kDecWaves * kVBytes
-                                                                               : kMergeFloats * 4;
+  static constexpr int kSmemBytes = (2 * kDecWaves * kVBytes > kMergeFloats * 4)
+                                        ? 2 * kDecWaves * kVBytes
+                                        : kMergeFloats * 4;
 };
 
 // Where the keys of one (row, KV head) unit live.  Page ids of 64
@@ -85,32 +90,21 @@ __device__ __forceinline__ uint32_t block_row(const RowCtx &c, int key0) {
   return ((uint32_t)page << c.page_shift) + (uint32_t)(key0 & ((1 << c.page_shift) - 1));
 }
 
-// K rows of a 32-key tile as QK A-operands.  kbase is the KV head's plane;
-// offsets are 32-bit (a head plane is below 4 GiB).  K and V are streamed
-// once per call; with kNT the loads are non-temporal, which pays when the
-// call keeps the whole chip streaming and costs latency when it does not.
 template <bool kNT>
 __device__ __forceinline__ u32x4 kv_load(const char *p) {
   if constexpr (kNT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
   return *reinterpret_cast<const u32x4 *>(p);
 }
 
+// The 32 K (or V) rows of a tile, whole rows: load i covers keys
+// i * kKeysPerLoad .. +kKeysPerLoad-1 of the tile, kLanesPerRow lanes of 16
+// bytes per row.  kbase/vbase is the KV head's plane; offsets are 32-bit (a
+// head plane is below 4 GiB).  K and V are streamed once per call; with kNT
+// the loads are non-temporal, which pays when the call keeps the whole chip
+// streaming and costs latency when it does not.
 template <int D, bool kNT>
-__device__ __forceinline__ void load_k(u32x4 (&k)[2][D / 32], const RowCtx &c, const char *kbase,
-                                       int kt, int lane) {
-  const int hl = lane & 15, lg = lane >> 4;
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const uint32_t off = (block_row(c, kt + 16 * b) + hl) * (2u * D) + 16u * lg;
-#pragma unroll
-    for (int ch = 0; ch < D / 32; ++ch)
-      k[b][ch] = kv_load<kNT>(kbase + off + 64u * ch);
-  }
-}
-
-template <int D, bool kNT>
-__device__ __forceinline__ void load_v(u32x4 (&v)[D / 16], const RowCtx &c, const char *vbase,
-                                       int kt, int lane) {
+__device__ __forceinline__ void load_rows(u32x4 (&v)[D / 16], const RowCtx &c, const char *vbase,
+                                          int kt, int lane) {
   using Gm = DecGeom<D>;
   const uint32_t row0 = block_row(c, kt), row1 = block_row(c, kt + 16);
   const uint32_t lane_off = (uint32_t)(lane / Gm::kLanesPerRow) * (2u * D) +
@@ -123,13 +117,14 @@ __device__ __forceinline__ void load_v(u32x4 (&v)[D / 16], const RowCtx &c, cons
   }
 }
 
-// Stage a tile's V rows in this wave's LDS tile; keys past the range become
-// zeros (0 * NaN would otherwise poison the accumulation).
-template <int D>
-__device__ __forceinline__ void store_v(const u32x4 (&v)[D / 16], char *vlds, int kt, int hi,
-                                        int lane) {
+// Stage a tile's rows in one of this wave's LDS tiles.  With kZeroTail,
+// keys past the range become zeros (for V: 0 * NaN would otherwise poison
+// the accumulation; K rows past the range only give scores that are masked).
+template <int D, bool kZeroTail>
+__device__ __forceinline__ void store_rows(const u32x4 (&v)[D / 16], char *vlds, int kt, int hi,
+                                           int lane) {
   using Gm = DecGeom<D>;
-  const bool tail = kt + kTileKeys > hi;
+  const bool tail = kZeroTail && kt + kTileKeys > hi;
 #pragma unroll
   for (int i = 0; i < Gm::kVLoads; ++i) {
     const int key = i * Gm::kKeysPerLoad + lane / Gm::kLanesPerRow;
@@ -141,19 +136,23 @@ __device__ __forceinline__ void store_v(const u32x4 (&v)[D / 16], char *vlds, in
 }
 
 template <int D>
-__device__ __forceinline__ void compute_tile(const u32x4 (&k)[2][D / 32], int kt, int hi,
-                                             const char *vlds, const bf16x8 *qop, float &m_run,
-                                             float &l_run, f32x4 *o, float scale_log2, int lane) {
+__device__ __forceinline__ void compute_tile(const char *klds, int kt, int hi, const char *vlds,
+                                             const bf16x8 *qop, float &m_run, float &l_run,
+                                             f32x4 *o, float scale_log2, int lane) {
   using Gm = DecGeom<D>;
   const int hl = lane & 15, lg = lane >> 4;
   const bool tail = kt + kTileKeys > hi;
 
-  // 1) scores for two 16-key blocks: S^T = K Q^T
+  // 1) scores for two 16-key blocks: S^T = K Q^T.  A-operand lane (hl, lg)
+  //    of step ch holds key hl (+16) at head_dim 32*ch + 8*lg .. +7.
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  const char *k_op = klds + hl * Gm::kRowStride + 16 * lg;
 #pragma unroll
   for (int ch = 0; ch < Gm::kDChunks; ++ch) {
-    s0 = mfma16x16x32(as_bf16x8(k[0][ch]), qop[ch], s0);
-    s1 = mfma16x16x32(as_bf16x8(k[1][ch]), qop[ch], s1);
+    const u32x4 k0 = *reinterpret_cast<const u32x4 *>(k_op + 64 * ch);
+    const u32x4 k1 = *reinterpret_cast<const u32x4 *>(k_op + 16 * Gm::kRowStride + 64 * ch);
+    s0 = mfma16x16x32(as_bf16x8(k0), qop[ch], s0);
+    s1 = mfma16x16x32(as_bf16x8(k1), qop[ch], s1);
   }
 
   // 2) online softmax, base 2.  Lane holds keys 4*lg+i (block 0) and
@@ -368,13 +367,14 @@ __device__ void decode_piece(const DecodeArgs &a, char *smem, int r, int g, int 
   const char *kbase = reinterpret_cast<const char *>(a.k_pool + (int64_t)g * a.plane_rows * D);
   const char *vbase = reinterpret_cast<const char *>(a.v_pool + (int64_t)g * a.plane_rows * D);
 
-  char *vlds = smem + wave * Gm::kVBytes;
+  char *klds = smem + (2 * wave) * Gm::kVBytes;
+  char *vlds = smem + (2 * wave + 1) * Gm::kVBytes;
 
   // The key range is walked in segments of at most 64 blocks (one page-id
   // window each; a single segment when the pages are contiguous).  Within a
-  // segment, a software pipeline keeps the next tile's K (other register set)
-  // and V (staging registers) in flight while the current tile is computed.
-  u32x4 ka[2][D / 32], kb[2][D / 32], vr[D / 16];
+  // segment, a software pipeline keeps the next tile's K and V (staging
+  // registers) in flight while the current tile, already in LDS, is computed.
+  u32x4 kr[D / 16], vr[D / 16];
   for (int seg_lo = lo; seg_lo < hi;) {
     const int seg_blk = seg_lo >> a.page_shift;
     const int seg_hi = c.contig ? hi
@@ -383,22 +383,15 @@ __device__ void decode_piece(const DecodeArgs &a, char *smem, int r, int g, int 
     c.hi = seg_hi;
     const int ntiles = (seg_hi - seg_lo + kTileKeys - 1) / kTileKeys;
     int t = wave;
-    load_v<D, kNT>(vr, c, vbase, seg_lo + t * kTileKeys, lane);
-    load_k<D, kNT>(ka, c, kbase, seg_lo + t * kTileKeys, lane);
+    load_rows<D, kNT>(vr, c, vbase, seg_lo + t * kTileKeys, lane);
+    load_rows<D, kNT>(kr, c, kbase, seg_lo + t * kTileKeys, lane);
     while (t < ntiles) {
-      store_v<D>(vr, vlds, seg_lo + t * kTileKeys, seg_hi, lane);
-      int tn = t + kDecWaves;
-      load_v<D, kNT>(vr, c, vbase, seg_lo + tn * kTileKeys, lane);
-      load_k<D, kNT>(kb, c, kbase, seg_lo + tn * kTileKeys, lane);
-      compute_tile<D>(ka, seg_lo + t * kTileKeys, seg_hi, vlds, qop, m_run, l_run, o,
-                      a.scale_log2, lane);
-      t = tn;
-      if (t >= ntiles) break;
-      store_v<D>(vr, vlds, seg_lo + t * kTileKeys, seg_hi, lane);
-      tn = t + kDecWaves;
-      load_v<D, kNT>(vr, c, vbase, seg_lo + tn * kTileKeys, lane);
-      load_k<D, kNT>(ka, c, kbase, seg_lo + tn * kTileKeys, lane);
-      compute_tile<D>(kb, seg_lo + t * kTileKeys, seg_hi, vlds, qop, m_run, l_run, o,
+      store_rows<D, true>(vr, vlds, seg_lo + t * kTileKeys, seg_hi, lane);
+      store_rows<D, false>(kr, klds, seg_lo + t * kTileKeys, seg_hi, lane);
+      const int tn = t + kDecWaves;
+      load_rows<D, kNT>(vr, c, vbase, seg_lo + tn * kTileKeys, lane);
+      load_rows<D, kNT>(kr, c, kbase, seg_lo + tn * kTileKeys, lane);
+      compute_tile<D>(klds, seg_lo + t * kTileKeys, seg_hi, vlds, qop, m_run, l_run, o,
                       a.scale_log2, lane);
       t = tn;
     }

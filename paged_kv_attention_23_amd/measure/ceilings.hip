@@ -12,6 +12,12 @@
 //                      each reading its unit's K and V rows (contiguous runs
 //                      given by the caller) in 32-key tiles dealt to waves in
 //                      turn, one tile in flight per wave
+//   ceil_paged_units   the same launch shape and tiles, with the keys found
+//                      the way paged decode finds them: the row's slot and
+//                      length from batch_idx / kv_len, then one load of the
+//                      page ids of its first 64 blocks, then each 16-key
+//                      block's rows through its page id (no arithmetic on
+//                      the data either)
 //   ceil_mfma          back-to-back 16x16x32 bf16 matrix instructions,
 //                      16 independent accumulators per wave, two waves per
 //                      SIMD (the dense bf16 rate of the instruction the
@@ -91,6 +97,62 @@ __global__ __launch_bounds__(256) void stream_units_kernel(const char *__restric
   if (x == key) sink[u & 1023] = x;
 }
 
+// Unit u = (row u / H_kv, KV head u % H_kv).  Rows in slot 0, beyond the
+// table or without keys exit; keys past 64 blocks are not read (the window
+// of one page-id load).  Rows are row_bytes apart in a head plane.
+__global__ __launch_bounds__(256) void paged_units_kernel(
+    const char *__restrict__ kpool, const char *__restrict__ vpool, uint64_t plane_bytes,
+    uint32_t row_bytes, int H_kv, const int32_t *__restrict__ page_table, int max_blocks,
+    int page_shift, int num_pages, int num_slots, const int32_t *__restrict__ batch_idx,
+    const int32_t *__restrict__ kv_len, uint32_t key, uint32_t *sink) {
+  const int u = blockIdx.x;
+  const int r = u / H_kv, g = u % H_kv;
+  const int s = batch_idx[r];
+  const int n = min(kv_len[r], min(max_blocks, 64) << page_shift);
+  if (s <= 0 || s >= num_slots || n <= 0) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int pwin = lane < max_blocks ? page_table[(int64_t)s * max_blocks + lane] : 0;
+  pwin = min(max(pwin, 0), num_pages - 1);
+  const uint64_t head = (uint64_t)g * plane_bytes;
+  const char *kb = kpool + head;
+  const char *vb = vpool + head;
+  const int ntiles = (n + 31) / 32;
+  const uint32_t in_page = (1u << page_shift) - 1u;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  u32x4 kr[8], vr[8];
+  // Load i of tile t covers keys 32t + 4i .. +3 (clamped to n-1): one
+  // 16-key block, hence one page id, for all 64 lanes.
+  auto issue = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int first = min(32 * t + 4 * i, n - 1);
+      const int page = __builtin_amdgcn_readlane(pwin, first >> page_shift);
+      const int k = min(32 * t + 4 * i + (lane >> 4), n - 1);
+      const uint32_t row = ((uint32_t)page << page_shift) + ((uint32_t)k & in_page);
+      const uint32_t off = row * row_bytes + (uint32_t)(lane & 15) * 16u;
+      kr[i] = ld_nt(reinterpret_cast<const u32x4 *>(kb + off));
+      vr[i] = ld_nt(reinterpret_cast<const u32x4 *>(vb + off));
+    }
+  };
+  int t = wave;
+  if (t < ntiles) issue(t);
+  while (t < ntiles) {
+    u32x4 k2[8], v2[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      k2[i] = kr[i];
+      v2[i] = vr[i];
+    }
+    const int tn = t + 4;
+    if (tn < ntiles) issue(tn);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc ^= k2[i] ^ v2[i];
+    t = tn;
+  }
+  const uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  if (x == key) sink[u & 1023] = x;
+}
+
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void mfma_kernel(int iters, float key, float *sink) {
   const float s = (float)(threadIdx.x & 7) * 0.001f;
@@ -131,6 +193,22 @@ int ceil_stream_units(const void *kpool, const void *vpool, uint64_t plane_bytes
   hipLaunchKernelGGL(stream_units_kernel, dim3(num_units), dim3(256), 0, (hipStream_t)stream,
                      (const char *)kpool, (const char *)vpool, plane_bytes, H_kv, units,
                      0x9e3779b9u, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// row_bytes: head_dim * 2 (16 lanes of 16 bytes read a row, so at most 256).
+int ceil_paged_units(const void *kpool, const void *vpool, uint64_t plane_bytes, uint32_t row_bytes,
+                     int H_kv, const int32_t *page_table, int max_blocks, int page_shift,
+                     int num_pages, int num_slots, const int32_t *batch_idx,
+                     const int32_t *kv_len, int batch, uint32_t *sink, void *stream) {
+  if (!kpool || !vpool || !page_table || !batch_idx || !kv_len || !sink || H_kv <= 0 ||
+      batch <= 0 || max_blocks <= 0 || num_pages <= 0 || page_shift < 4 || row_bytes != 256u ||
+      plane_bytes > 0xffffffffull || (uint64_t)num_pages << page_shift > plane_bytes / row_bytes)
+    return -1;
+  hipLaunchKernelGGL(paged_units_kernel, dim3((unsigned)batch * (unsigned)H_kv), dim3(256), 0,
+                     (hipStream_t)stream, (const char *)kpool, (const char *)vpool, plane_bytes,
+                     row_bytes, H_kv, page_table, max_blocks, page_shift, num_pages, num_slots,
+                     batch_idx, kv_len, 0x9e3779b9u, sink);
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
