@@ -258,7 +258,7 @@ int paged_decode_attn_append(const void *q, const void *k_new, const void *v_new
  *   out          bf16 [total_len][num_q_heads][head_dim]
  *   lse          fp32 [total_len][num_q_heads] (natural log)
  *
- * total_len == 0 is a valid no-op.  Requirements: head_dim 128, num_q_heads a
+ * total_len == 0 is a valid no-op.  Requirements: head_dim 64 or 128, num_q_heads a
  * multiple of num_kv_heads with at most 16 query heads per KV head, scale
  * finite and > 0.
  */

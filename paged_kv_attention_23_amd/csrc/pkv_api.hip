@@ -471,7 +471,8 @@ static int prefill_common(const char *who, const void *q, const void *k, const v
                           const int32_t *prefix_lens, void *stream) {
   if (total_len < 0 || num_docs < 0)
     return fail(PKV_E_SHAPE, "total_len and num_docs must be >= 0 (got %d, %d)", total_len, num_docs);
-  if (head_dim != 128) return fail(PKV_E_SHAPE, "%s supports head_dim 128 (got %d)", who, head_dim);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_E_SHAPE, "%s: head_dim must be 64 or 128 (got %d)", who, head_dim);
   if (num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
     return fail(PKV_E_SHAPE, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
                 num_q_heads, num_kv_heads);
@@ -509,6 +510,7 @@ static int prefill_common(const char *who, const void *q, const void *k, const v
   a.H_q = num_q_heads;
   a.H_kv = num_kv_heads;
   a.G = num_q_heads / num_kv_heads;
+  a.D = head_dim;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.out = (uint16_t *)out;
   a.lse = lse;

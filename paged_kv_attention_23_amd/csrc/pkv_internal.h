@@ -58,6 +58,7 @@ struct PrefillArgs {
   const int32_t *prefix_lens;      // [num_docs] cached tokens before each chunk; NULL: none
   int64_t plane_rows;
   int32_t num_pages, page_shift, num_slots, max_blocks;
+  int32_t D;                       // head_dim: 64 or 128
 };
 
 // Debug checks (pkv_validate_decode / pkv_validate_prefill).  Decode: rows

@@ -44,21 +44,32 @@ namespace pkv {
 #ifndef PKV_PF_WPE
 #define PKV_PF_WPE 2
 #endif
-constexpr int kPfD = 128;
 constexpr int kPfWaves = 4;
 constexpr int kPfThreads = kPfWaves * kWave;
 constexpr int kQB = PKV_PF_QB;                       // 16-column blocks per wave
 constexpr int kPfRows = 16 * kQB * kPfWaves;         // (head, query) rows per workgroup
 constexpr int kPfBN = PKV_PF_BN;                     // keys per LDS stage (multiple of 32)
 constexpr int kHalves = kPfBN / 32;                  // 32-key steps per stage
-constexpr int kPfRowStride = 2 * kPfD + 16;          // bytes per K row in LDS
-constexpr int kPfVRowStride = 2 * kPfD + 64;         // bytes per V row in LDS
-constexpr int kPfKTileBytes = kPfBN * kPfRowStride;  // one K stage
-constexpr int kPfStageBytes = kPfKTileBytes + kPfBN * kPfVRowStride;  // K, then V
-constexpr int kPfSmem = 2 * kPfStageBytes;           // 2 stages
-constexpr int kPfLoads = kPfBN * (2 * kPfD / 16) / kPfThreads;  // 16-byte pieces per thread per tensor
-static_assert(kPfThreads / 16 == 16, "a stage piece spans 16 keys, the smallest page");
 constexpr float kLazy = 8.f;                         // lazy-rescale threshold, log2 units
+
+// Layout of one head_dim (64 or 128).  A K/V row of D bf16 values is D/8
+// 16-byte pieces; one pass of the workgroup's threads over a stage covers
+// kRowsPerPass consecutive key rows (16 at D = 128, 32 at D = 64).  LDS rows
+// are padded (K by 16 bytes, V by 64) so that the 16 addresses of an operand
+// read group fall in distinct banks at either head_dim.
+template <int D>
+struct PfGeom {
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+  static constexpr int kRowStride = 2 * D + 16;               // bytes per K row in LDS
+  static constexpr int kVRowStride = 2 * D + 64;              // bytes per V row in LDS
+  static constexpr int kKTileBytes = kPfBN * kRowStride;      // one K stage
+  static constexpr int kStageBytes = kKTileBytes + kPfBN * kVRowStride;  // K, then V
+  static constexpr int kSmem = 2 * kStageBytes;               // 2 stages
+  static constexpr int kPieces = D / 8;                       // 16-byte pieces per row
+  static constexpr int kRowsPerPass = kPfThreads / kPieces;   // rows per pass of the workgroup
+  static constexpr int kLoads = kPfBN / kRowsPerPass;         // passes per stage
+  static_assert(kRowsPerPass % 16 == 0 && kPfBN % kRowsPerPass == 0, "passes are 16-key aligned");
+};
 
 struct PfTile {
   int doc, doc_start, doc_end, q_lo, q_hi;
@@ -116,12 +127,15 @@ __device__ bool find_tile(const int32_t *cu, int num_docs, int L, int QT, int qt
   return false;
 }
 
-template <bool kFused, bool kPrefix>
+template <int D, bool kFused, bool kPrefix>
 __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(PKV_PF_WPE)))
 void prefill_kernel(PrefillArgs a) {
   static_assert(kFused || !kPrefix, "a paged prefix comes with the chunk's scatter");
-  __shared__ __attribute__((aligned(16))) char smem[kPfSmem];
-  constexpr int D = kPfD;
+  using Gm = PfGeom<D>;
+  constexpr int kPfRowStride = Gm::kRowStride, kPfVRowStride = Gm::kVRowStride;
+  constexpr int kPfKTileBytes = Gm::kKTileBytes, kPfStageBytes = Gm::kStageBytes;
+  constexpr int kPieces = Gm::kPieces, kRowsPerPass = Gm::kRowsPerPass, kPfLoads = Gm::kLoads;
+  __shared__ __attribute__((aligned(16))) char smem[Gm::kSmem];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int hl = lane & 15, lg = lane >> 4;
@@ -161,8 +175,8 @@ void prefill_kernel(PrefillArgs a) {
           if (hh >= G || qq >= tl.q_hi) continue;
           const int64_t rh = (int64_t)qq * a.H_q + g * G + hh;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<u32x4 *>(a.out + rh * kPfD + 32 * lg + 8 * i) = u32x4{0u, 0u, 0u, 0u};
+          for (int i = 0; i < D / 32; ++i)  // lane lg: the D/4 values from (D/4)*lg
+            *reinterpret_cast<u32x4 *>(a.out + rh * D + (D / 4) * lg + 8 * i) = u32x4{0u, 0u, 0u, 0u};
           if (lg == 0) a.lse[rh] = -INFINITY;
         }
         return;
@@ -195,22 +209,22 @@ void prefill_kernel(PrefillArgs a) {
     }
   }
 
-  // Cooperative stage loads: piece p = threadIdx.x + 256*i -> key row p/16, 16-byte column p%16.
+  // Cooperative stage loads: piece p = threadIdx.x + 256*i -> key row p/(D/8), 16-byte column p%(D/8).
   // Keys past k_end (last stage only) are clamped to the last key: they lie
   // past every row's position, so their scores are masked and their
   // probabilities are exactly 0 against finite values.
   const int64_t row_stride = (int64_t)a.H_kv * D;  // elements between consecutive tokens
   const uint32_t row_bytes = (uint32_t)row_stride * 2u;  // < 2^24, checked on the host
-  const uint32_t col_bytes = (threadIdx.x & 15) * 16u;
-  const int row0 = threadIdx.x >> 4;                    // stage row of piece 0
+  const uint32_t col_bytes = (threadIdx.x % kPieces) * 16u;
+  const int row0 = threadIdx.x / kPieces;               // stage row of piece 0
   const uint16_t *kg = a.k + (int64_t)g * D;
   const uint16_t *vg = a.v + (int64_t)g * D;
   const int32_t *pt_row = kFused ? a.page_table + (int64_t)slot * a.max_blocks : nullptr;
   // Cached prefix: page ids of the document's first 64 blocks, one per lane,
-  // loaded once.  In a stage inside the prefix, piece i covers the 16 keys
-  // key0 + 16*i .. +15, which lie in one page (pages hold >= 16 keys and the
-  // pieces are 16-aligned), so each piece needs one page id (a lane read)
-  // and one uniform base.
+  // loaded once.  In a stage inside the prefix, pass i covers the keys
+  // key0 + kRowsPerPass*i ..; each 16-key group of them lies in one page
+  // (pages hold >= 16 keys and the groups are 16-aligned), so each group
+  // needs one page id (a lane read) and one uniform base.
   int pwin = 0;
   if constexpr (kPrefix) {
     const int nblk = (prefix + (1 << a.page_shift) - 1) >> a.page_shift;
@@ -222,12 +236,25 @@ void prefill_kernel(PrefillArgs a) {
     const int key0 = s * kPfBN;  // position of the stage's first key
     if (kPrefix && key0 + kPfBN <= prefix) {
       // Whole stage in the cached prefix: one page per 16-key piece.
-      const uint32_t off = (uint32_t)row0 * (uint32_t)(D * 2) + col_bytes;
+      const int grow = kRowsPerPass == 16 ? row0 : (row0 & 15);  // the lane's row in its 16-key group
+      const uint32_t off = (uint32_t)grow * (uint32_t)(D * 2) + col_bytes;
 #pragma unroll
       for (int i = 0; i < kPfLoads; ++i) {
-        const int key = key0 + (kPfThreads / 16) * i;  // the piece's first key
-        const int blk = key >> a.page_shift;
-        int page = blk < kWave ? __builtin_amdgcn_readlane(pwin, blk) : pt_row[blk];
+        int key = key0 + kRowsPerPass * i;  // first key of the lane's 16-key group
+        int page;
+        if constexpr (kRowsPerPass == 16) {
+          const int blk = key >> a.page_shift;
+          page = blk < kWave ? __builtin_amdgcn_readlane(pwin, blk) : pt_row[blk];
+        } else {
+          page = 0;
+#pragma unroll
+          for (int j = 0; j < kRowsPerPass / 16; ++j) {  // one uniform page id per group
+            const int blk = (key + 16 * j) >> a.page_shift;
+            const int pj = blk < kWave ? __builtin_amdgcn_readlane(pwin, blk) : pt_row[blk];
+            if ((row0 >> 4) == j) page = pj;
+          }
+          key += 16 * (row0 >> 4);
+        }
         page = min(max(page, 0), a.num_pages - 1);
         const int64_t first = ((int64_t)g * a.plane_rows + ((int64_t)page << a.page_shift) +
                                (key & ((1 << a.page_shift) - 1))) * D;
@@ -243,7 +270,7 @@ void prefill_kernel(PrefillArgs a) {
       const int last = k_end - 1 - key0;  // last live row of the stage
 #pragma unroll
       for (int i = 0; i < kPfLoads; ++i) {
-        const int r = min(row0 + (kPfThreads / 16) * i, last);
+        const int r = min(row0 + kRowsPerPass * i, last);
         const uint32_t off = __umul24((uint32_t)r, row_bytes) + col_bytes;
         stk[i] = *reinterpret_cast<const u32x4 *>(kbs + off);
         stv[i] = *reinterpret_cast<const u32x4 *>(vbs + off);
@@ -252,16 +279,16 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int i = 0; i < kPfLoads; ++i) {
         const int p = threadIdx.x + kPfThreads * i;
-        const int key = min(key0 + (p >> 4), k_end - 1);
+        const int key = min(key0 + p / kPieces, k_end - 1);
         if (key < prefix) {                 // cached prefix: through the page table
           int page = pt_row[key >> a.page_shift];
           page = min(max(page, 0), a.num_pages - 1);
           const int64_t row = (int64_t)g * a.plane_rows + ((int64_t)page << a.page_shift) +
                               (key & ((1 << a.page_shift) - 1));
-          stk[i] = *reinterpret_cast<const u32x4 *>(a.k_pool + row * D + (p & 15) * 8);
-          stv[i] = *reinterpret_cast<const u32x4 *>(a.v_pool + row * D + (p & 15) * 8);
+          stk[i] = *reinterpret_cast<const u32x4 *>(a.k_pool + row * D + (p % kPieces) * 8);
+          stv[i] = *reinterpret_cast<const u32x4 *>(a.v_pool + row * D + (p % kPieces) * 8);
         } else {                            // this document's packed rows
-          const int64_t off = (int64_t)(tl.doc_start + key - prefix) * row_stride + (p & 15) * 8;
+          const int64_t off = (int64_t)(tl.doc_start + key - prefix) * row_stride + (p % kPieces) * 8;
           stk[i] = *reinterpret_cast<const u32x4 *>(kg + off);
           stv[i] = *reinterpret_cast<const u32x4 *>(vg + off);
         }
@@ -271,7 +298,7 @@ void prefill_kernel(PrefillArgs a) {
       if (scatter) {
 #pragma unroll
         for (int i = 0; i < kPfLoads; ++i) {
-          const int pos = key0 + row0 + (kPfThreads / 16) * i;
+          const int pos = key0 + row0 + kRowsPerPass * i;
           const int blk = pos >> a.page_shift;
           spage[i] = (pos >= prefix && pos < k_end && blk < a.max_blocks) ? pt_row[blk] : 0;
         }
@@ -283,12 +310,12 @@ void prefill_kernel(PrefillArgs a) {
     for (int i = 0; i < kPfLoads; ++i) {
       const int p = threadIdx.x + kPfThreads * i;
       if (spage[i] > 0 && spage[i] < a.num_pages) {
-        const int pos = s * kPfBN + (p >> 4);
+        const int pos = s * kPfBN + p / kPieces;
         const int64_t row = (int64_t)g * a.plane_rows + ((int64_t)spage[i] << a.page_shift) +
                             (pos & ((1 << a.page_shift) - 1));
         // whole 256-byte rows, not read again here: past the caches
-        __builtin_nontemporal_store(stk[i], reinterpret_cast<u32x4 *>(a.k_pool + row * D + (p & 15) * 8));
-        __builtin_nontemporal_store(stv[i], reinterpret_cast<u32x4 *>(a.v_pool + row * D + (p & 15) * 8));
+        __builtin_nontemporal_store(stk[i], reinterpret_cast<u32x4 *>(a.k_pool + row * D + (p % kPieces) * 8));
+        __builtin_nontemporal_store(stv[i], reinterpret_cast<u32x4 *>(a.v_pool + row * D + (p % kPieces) * 8));
       }
     }
   };
@@ -298,8 +325,8 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < kPfLoads; ++i) {
       const int p = threadIdx.x + kPfThreads * i;
-      *reinterpret_cast<u32x4 *>(kb + (p >> 4) * kPfRowStride + (p & 15) * 16) = stk[i];
-      *reinterpret_cast<u32x4 *>(vb + (p >> 4) * kPfVRowStride + (p & 15) * 16) = stv[i];
+      *reinterpret_cast<u32x4 *>(kb + (p / kPieces) * kPfRowStride + (p % kPieces) * 16) = stk[i];
+      *reinterpret_cast<u32x4 *>(vb + (p / kPieces) * kPfVRowStride + (p % kPieces) * 16) = stv[i];
     }
   };
 
@@ -443,7 +470,7 @@ void prefill_kernel(PrefillArgs a) {
 
   // Normalise and write: lane holds O[row][d = 32*(t/2) + 8*lg + 4*(t%2) + i]
   // in o[qb][t][i], so steps 2c and 2c+1 are 8 contiguous values and the four
-  // lanes of a row write 64 contiguous bytes per store.
+  // lanes of a row write 64 contiguous bytes per store (D/32 stores).
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
     float l = l_run[qb];
@@ -454,7 +481,7 @@ void prefill_kernel(PrefillArgs a) {
     const int64_t rh = (int64_t)col_q[qb] * a.H_q + col_head[qb];
     uint16_t *orow = a.out + rh * D + 8 * lg;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {  // 16-byte piece c: d = 32*c + 8*lg + 0..7 = steps 2c, 2c+1
+    for (int c = 0; c < D / 32; ++c) {  // 16-byte piece c: d = 32*c + 8*lg + 0..7 = steps 2c, 2c+1
       const f32x4 a0 = o[qb][2 * c], a1 = o[qb][2 * c + 1];
       const u32x4 w = {pack_bf16x2(a0[0] * inv, a0[1] * inv), pack_bf16x2(a0[2] * inv, a0[3] * inv),
                        pack_bf16x2(a1[0] * inv, a1[1] * inv), pack_bf16x2(a1[2] * inv, a1[3] * inv)};
@@ -470,12 +497,23 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
   // Sum over documents of ceil(n_d / QT) is at most ceil(L / QT) + num_docs.
   const int64_t tiles = ((int64_t)a.L + QT - 1) / QT + a.num_docs;
   const dim3 grid((unsigned)(tiles * a.H_kv));
-  if (a.prefix_lens)
-    hipLaunchKernelGGL((prefill_kernel<true, true>), grid, dim3(kPfThreads), 0, stream, a);
-  else if (a.k_pool)
-    hipLaunchKernelGGL((prefill_kernel<true, false>), grid, dim3(kPfThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((prefill_kernel<false, false>), grid, dim3(kPfThreads), 0, stream, a);
+  if (a.D == 64) {
+    if (a.prefix_lens)
+      hipLaunchKernelGGL((prefill_kernel<64, true, true>), grid, dim3(kPfThreads), 0, stream, a);
+    else if (a.k_pool)
+      hipLaunchKernelGGL((prefill_kernel<64, true, false>), grid, dim3(kPfThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((prefill_kernel<64, false, false>), grid, dim3(kPfThreads), 0, stream, a);
+  } else if (a.D == 128) {
+    if (a.prefix_lens)
+      hipLaunchKernelGGL((prefill_kernel<128, true, true>), grid, dim3(kPfThreads), 0, stream, a);
+    else if (a.k_pool)
+      hipLaunchKernelGGL((prefill_kernel<128, true, false>), grid, dim3(kPfThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((prefill_kernel<128, false, false>), grid, dim3(kPfThreads), 0, stream, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

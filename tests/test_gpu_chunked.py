@@ -39,7 +39,7 @@ def _run(c, kd=None, vd=None):
 
 
 CASES = [
-    # (seed, prefix_lens, chunk_lens, H_q, H_kv, page_size, slots)
+    # (seed, prefix_lens, chunk_lens, H_q, H_kv, page_size, slots[, head_dim])
     (91, [0, 1, 63, 64, 65, 200, 700], [1, 33, 64, 100, 5, 128, 300], 32, 8, 16, None),
     (92, [5, 0, 130, 1000], [70, 9, 1, 40], 16, 2, 64, None),               # G = 8
     (93, [300, 40, 17], [0, 64, 200], 16, 1, 128, None),                    # G = 16, empty chunk
@@ -50,15 +50,20 @@ CASES = [
     # prefixes past 64 pages of 64 tokens (page ids beyond the per-tile window of 64)
     (99, [4700, 4160, 4096, 4095], [40, 64, 3, 1], 16, 2, 64, None),
     (100, [700, 257, 256, 255], [33, 100, 1, 64], 32, 8, 256, None),        # page_size 256
+    # head_dim 64: a stage pass covers 32 keys, i.e. two 16-token pages
+    (191, [0, 1, 63, 64, 65, 200, 700], [1, 33, 64, 100, 5, 128, 300], 32, 8, 16, None, 64),
+    (192, [1100, 1024, 1023, 40], [40, 64, 3, 1], 16, 2, 16, [1, 0, 3, 4], 64),  # past 64 pages
+    (193, [700, 257, 256, 255], [33, 100, 1, 64], 32, 8, 256, None, 64),
 ]
 
 
 @pytest.mark.parametrize("spec", CASES, ids=[f"seed{s[0]}" for s in CASES])
 def test_chunked_prefill(spec):
-    seed, prefix, chunk, H_q, H_kv, ps, slots = spec
-    print(f"chunked prefill seed={seed}", flush=True)
+    seed, prefix, chunk, H_q, H_kv, ps, slots = spec[:7]
+    D = spec[7] if len(spec) > 7 else 128
+    print(f"chunked prefill seed={seed} D={D}", flush=True)
     c = make_chunked_prefill_case(name="chunk", seed=seed, prefix_lens=prefix, chunk_lens=chunk,
-                                  H_q=H_q, H_kv=H_kv, D=128, page_size=ps, slots=slots)
+                                  H_q=H_q, H_kv=H_kv, D=D, page_size=ps, slots=slots)
     kp, vp, out_ref, lse_ref = _expected(c)
     out, lse, kb, vb = _run(c)
     check_close(out, lse, out_ref, lse_ref, f"chunked seed{seed}")

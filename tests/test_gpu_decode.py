@@ -152,8 +152,6 @@ def _sched(splits):
 @pytest.mark.parametrize("mode", list(MODES))
 def test_decode_parity(cfg, splits, mode):
     _print_case(f"decode cfg{cfg} splits={splits} mode={mode}")
-    if cfg == 4 and mode == "walk" and splits in (3, 7):
-        pytest.skip("covered by the other split counts")
     d = _dev(cfg)
     _, _, out_ref, lse_ref = _ref(cfg)
     S, extra = _sched(splits)

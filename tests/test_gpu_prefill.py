@@ -64,6 +64,26 @@ def test_prefill_edge_shapes(spec):
     check_close(out, lse, out_ref, lse_ref, f"prefill seed{seed}")
 
 
+EDGE_D64 = [
+    # (seed, doc_lens, H_q, H_kv) at head_dim 64: one pass of the stage loads covers 32 keys
+    (161, [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129], 32, 8),    # G = 4, tile edges
+    (162, [300, 1, 17, 0], 16, 1),                                   # G = 16, an empty document
+    (163, [1000, 7], 8, 8),                                          # G = 1, one long document
+]
+
+
+@pytest.mark.parametrize("spec", EDGE_D64, ids=[f"seed{s[0]}" for s in EDGE_D64])
+def test_prefill_head_dim_64(spec):
+    seed, lens, H_q, H_kv = spec
+    print(f"prefill D=64 seed={seed}", flush=True)
+    pc = make_prefill_case(name="d64", seed=seed, doc_lens=lens, H_q=H_q, H_kv=H_kv, D=64,
+                           page_size=128, num_pages=64, max_blocks=8)
+    out_ref, lse_ref = oracle.prefill_case(pc)
+    out, lse = _run(pc)
+    assert out.shape == (pc.L, H_q, 64)
+    check_close(out, lse, out_ref, lse_ref, f"prefill D=64 seed{seed}")
+
+
 def test_prefill_growing_scores():
     """Key magnitudes grow along each document, with spikes late in it, so the running
     reference max of a query row moves again and again inside its tile: the path that
@@ -184,11 +204,13 @@ def test_prefill_fused_scatter_64_docs():
 
 
 FUSED_EDGE = [
-    # (seed, doc_lens, page_size, max_blocks)
-    (71, [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129], 16, 16),   # many pages per document
-    (72, [0, 5, 0, 70, 0], 32, 4),                                   # empty documents
-    (73, [300, 1, 17], 64, 8),
-    (74, [1000], 128, 8),                                            # one long document
+    # (seed, doc_lens, page_size, max_blocks, head_dim)
+    (71, [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129], 16, 16, 128),   # many pages per document
+    (72, [0, 5, 0, 70, 0], 32, 4, 128),                                   # empty documents
+    (73, [300, 1, 17], 64, 8, 128),
+    (74, [1000], 128, 8, 128),                                            # one long document
+    (171, [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129], 16, 16, 64),    # head_dim 64
+    (172, [300, 1, 17, 1000], 128, 8, 64),
 ]
 
 
@@ -197,9 +219,9 @@ def test_prefill_fused_scatter_edges(spec):
     """Shapes as above plus the skip rules: a document in slot 0, a document whose later
     blocks are unmapped (page 0), a slot beyond the table, and a document longer than
     the table (blocks past max_blocks)."""
-    seed, lens, ps, mb = spec
+    seed, lens, ps, mb, D = spec
     print(f"prefill fused edge seed={seed}", flush=True)
-    pc = make_prefill_case(name="fedge", seed=seed, doc_lens=lens, H_q=32, H_kv=8, D=128,
+    pc = make_prefill_case(name="fedge", seed=seed, doc_lens=lens, H_q=32, H_kv=8, D=D,
                            page_size=ps, num_pages=sum(-(-n // ps) for n in lens) + 4,
                            max_blocks=max(-(-max(lens) // ps), 1))
     out_ref, lse_ref = oracle.prefill_case(pc)

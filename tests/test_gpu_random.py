@@ -80,9 +80,10 @@ def test_random_chunked_prefill(seed):
     chunk = [int(x) for x in rng.integers(0, 200, B)]
     if rng.random() < 0.3:
         prefix = [0] * B
-    print(f"random chunked seed={seed} B={B} G={H_q // H_kv} ps={ps}", flush=True)
+    D = int(rng.choice([64, 128]))
+    print(f"random chunked seed={seed} B={B} G={H_q // H_kv} D={D} ps={ps}", flush=True)
     c = make_chunked_prefill_case(name="rand", seed=seed, prefix_lens=prefix, chunk_lens=chunk,
-                                  H_q=H_q, H_kv=H_kv, D=128, page_size=ps, slots=slots)
+                                  H_q=H_q, H_kv=H_kv, D=D, page_size=ps, slots=slots)
     if c.L == 0:
         pytest.skip("empty draw")
     kp, vp = oracle.append_pages(c.k_pool, c.v_pool, c.num_pages, ps, c.page_table, c.batch_idx,

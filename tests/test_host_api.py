@@ -143,7 +143,8 @@ def test_append_checks(lib):
 def test_prefill_checks(lib):
     f = lib.packed_prefill_attn
     assert f(0, 0, 0, 0, 0, 0, 32, 8, 128, 0.1, 0, 0, 0) == 0               # empty: no-op
-    assert f(FAKE, FAKE, FAKE, FAKE, 1, 10, 32, 8, 64, 0.1, FAKE, FAKE, 0) == -2
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 10, 32, 8, 96, 0.1, FAKE, FAKE, 0) == -2      # head_dim
+    assert "head_dim" in B.last_error()
     assert f(FAKE, FAKE, FAKE, FAKE, 1, 10, 30, 8, 128, 0.1, FAKE, FAKE, 0) == -2
     assert f(FAKE, FAKE, FAKE, FAKE, 0, 10, 32, 8, 128, 0.1, FAKE, FAKE, 0) == -2
     assert f(FAKE, 0, FAKE, FAKE, 1, 10, 32, 8, 128, 0.1, FAKE, FAKE, 0) == -1
