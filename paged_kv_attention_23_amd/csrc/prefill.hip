@@ -51,6 +51,7 @@ constexpr int kPfRows = 16 * kQB * kPfWaves;         // (head, query) rows per w
 constexpr int kPfBN = PKV_PF_BN;                     // keys per LDS stage (multiple of 32)
 constexpr int kHalves = kPfBN / 32;                  // 32-key steps per stage
 constexpr float kLazy = 8.f;                         // lazy-rescale threshold, log2 units
+constexpr float kLazyWeight = 256.f;                 // 2^kLazy: the largest weight a step keeps
 
 // Layout of one head_dim (64 or 128).  A K/V row of D bf16 values is D/8
 // 16-byte pieces; one pass of the workgroup's threads over a stage covers
@@ -412,21 +413,24 @@ void prefill_kernel(PrefillArgs a) {
             if (off > lim) x[i] = -INFINITY;
           }
         }
-        // Speculative weights against the current reference point m_run; a
-        // lane-local max tests whether it must move (some lane's scores
-        // exceed it by more than kLazy, in log2 units).  The test and the
-        // new reference are those of the column max (max commutes with the
-        // positive scale), so only the rare step that moves it recomputes.
-        float lm = x[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) lm = fmaxf(lm, x[i]);
+        // Speculative weights against the current reference point m_run.  The
+        // reference must move only when some weight exceeds 2^kLazy; every
+        // weight is at most its lane's sum, so the sum the step needs anyway
+        // is the test (it may fire on a step that could have stayed, never
+        // miss one).  The rare step that moves it takes the column max (max
+        // commutes with the positive scale) and recomputes.
         float p[8], ps = 0.f;
         if (!first) {
           const float m_use = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
 #pragma unroll
           for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(x[i], a.scale_log2, -m_use));
+#pragma unroll
+          for (int i = 0; i < 8; ++i) ps += p[i];
         }
-        if (first || __any(lm * a.scale_log2 > m_run[qb] + kLazy)) {
+        if (first || __any(!(ps <= kLazyWeight))) {
+          float lm = x[0];
+#pragma unroll
+          for (int i = 1; i < 8; ++i) lm = fmaxf(lm, x[i]);
           float mt = max_xor16(lm);
           mt = max_xor32(mt);
           mt *= a.scale_log2;
@@ -441,9 +445,10 @@ void prefill_kernel(PrefillArgs a) {
           const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
 #pragma unroll
           for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(x[i], a.scale_log2, -m_use));
-        }
+          ps = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ps += p[i];
+          for (int i = 0; i < 8; ++i) ps += p[i];
+        }
         l_run[qb] += ps;
         const u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                           pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
