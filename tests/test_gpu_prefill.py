@@ -173,6 +173,31 @@ def test_prefill_then_decode_through_pages():
                 "decode vs prefill (GPU both)")
 
 
+def test_prefill_long_document_sampled_rows():
+    """A 16384-token document (512 query tiles, 16384-key ranges) packed with two short ones:
+    the GPU computes every row, the oracle a sample of rows one by one, each as the decode
+    of that query over its document's keys [0, position] written into pages."""
+    print("prefill long document, sampled rows", flush=True)
+    lens = [16384, 37, 1000]
+    pc = make_prefill_case(name="long", seed=66, doc_lens=lens, H_q=32, H_kv=8, D=128,
+                           page_size=128, num_pages=sum(-(-n // 128) for n in lens) + 4,
+                           max_blocks=128)
+    out, lse = _run(pc)
+    rng = np.random.default_rng(66)
+    rows = sorted(set([0, 1, 31, 32, 33, 127, 128, 4095, 4096, 8191, 8192, 12000, 16383,
+                       16384, 16420, 16421, 17420] + [int(x) for x in rng.integers(0, pc.L, 24)]))
+    rows = np.asarray(rows, dtype=np.int64)
+    kp0 = np.full((pc.H_kv, pc.num_pages * pc.page_size, pc.D), BF16_NAN, np.uint16)
+    kp, vp = oracle.append_pages(kp0, kp0.copy(), pc.num_pages, pc.page_size, pc.page_table,
+                                 pc.batch_idx, pc.input_pos, pc.k, pc.v)
+    out_ref, lse_ref = oracle.decode(pc.q[rows], kp, vp, pc.num_pages, pc.page_size, pc.page_table,
+                                     pc.batch_idx[rows], np.zeros(len(rows), np.int32),
+                                     (pc.input_pos[rows] + 1).astype(np.int32), pc.scale)
+    idx = torch.from_numpy(rows).cuda()
+    check_close(out.index_select(0, idx), lse.index_select(0, idx), out_ref, lse_ref,
+                "prefill long document (sampled rows)")
+
+
 # ----------------------------------------------------------------------------- fused scatter
 def _run_fused(pc, doc_slots, kp0, vp0, page_table=None):
     kd, vd = dev_bf16(kp0), dev_bf16(vp0)
