@@ -424,8 +424,7 @@ void prefill_kernel(PrefillArgs a) {
           const float m_use = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
 #pragma unroll
           for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(x[i], a.scale_log2, -m_use));
-#pragma unroll
-          for (int i = 0; i < 8; ++i) ps += p[i];
+          ps = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
         }
         if (first || __any(!(ps <= kLazyWeight))) {
           float lm = x[0];
@@ -445,9 +444,7 @@ void prefill_kernel(PrefillArgs a) {
           const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
 #pragma unroll
           for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(x[i], a.scale_log2, -m_use));
-          ps = 0.f;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) ps += p[i];
+          ps = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
         }
         l_run[qb] += ps;
         const u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
