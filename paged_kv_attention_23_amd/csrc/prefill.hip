@@ -331,12 +331,13 @@ void prefill_kernel(PrefillArgs a) {
     }
   };
 
-  float m_run[kQB], l_run[kQB];
+  float m_run[kQB], l_run[kQB], neg_m[kQB];  // neg_m: -m_run, or 0 while m_run is -inf
   f32x4 o[kQB][D / 16];
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
     m_run[qb] = -INFINITY;
     l_run[qb] = 0.f;
+    neg_m[qb] = 0.f;
   }
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb)
@@ -421,9 +422,8 @@ void prefill_kernel(PrefillArgs a) {
         // commutes with the positive scale) and recomputes.
         float p[8], ps = 0.f;
         if (!first) {
-          const float m_use = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(x[i], a.scale_log2, -m_use));
+          for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(x[i], a.scale_log2, neg_m[qb]));
           ps = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
         }
         if (first || __any(!(ps <= kLazyWeight))) {
@@ -441,9 +441,9 @@ void prefill_kernel(PrefillArgs a) {
             for (int t = 0; t < D / 16; ++t) o[qb][t] *= alpha;
           }
           m_run[qb] = m_new;
-          const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+          neg_m[qb] = (m_new == -INFINITY) ? 0.f : -m_new;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(x[i], a.scale_log2, -m_use));
+          for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(x[i], a.scale_log2, neg_m[qb]));
           ps = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
         }
         l_run[qb] += ps;
