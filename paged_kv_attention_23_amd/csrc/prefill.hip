@@ -94,6 +94,20 @@ __device__ __forceinline__ int doc_hi(const int32_t *cu, int d, int lo, int L) {
   return min(max(cu[d + 1], lo), L);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave, in registers: four
+// row shifts give the sums within each 16-lane row, then the last lane of
+// row 0 is added to row 1 and of row 2 to row 3, and lane 31 to rows 2 and
+// 3.  Lanes whose source lies outside the row take 0.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
 __device__ bool find_tile(const int32_t *cu, int num_docs, int L, int QT, int qt_shift, int tile,
                           int lane, PfTile &out) {
   int base = 0;  // tiles of the documents before this chunk
@@ -104,17 +118,12 @@ __device__ bool find_tile(const int32_t *cu, int num_docs, int L, int QT, int qt
       const int lo = doc_lo(cu, d, L);
       t = ceil_div_qt(doc_hi(cu, d, lo, L) - lo, QT, qt_shift);
     }
-    int incl = t;  // inclusive prefix sum of tile counts over the chunk
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int u = __shfl_up(incl, off, kWave);
-      if (lane >= off) incl += u;
-    }
+    const int incl = wave_incl_scan(t);  // inclusive prefix sum of tile counts over the chunk
     const uint64_t hit = __ballot(base + incl > tile);
     if (hit) {
-      const int j = __builtin_ctzll(hit);
+      const int j = __builtin_ctzll(hit);  // uniform
       const int dd = d0 + j;
-      const int end = base + __shfl(incl, j, kWave);
+      const int end = base + __builtin_amdgcn_readlane(incl, j);
       const int qt = end - 1 - tile;  // query tile inside the document, last first
       out.doc = dd;
       out.doc_start = doc_lo(cu, dd, L);
@@ -123,7 +132,7 @@ __device__ bool find_tile(const int32_t *cu, int num_docs, int L, int QT, int qt
       out.q_hi = min(out.doc_end, out.q_lo + QT);
       return true;
     }
-    base += __shfl(incl, kWave - 1, kWave);
+    base += __builtin_amdgcn_readlane(incl, kWave - 1);
   }
   return false;
 }
