@@ -523,20 +523,32 @@ __device__ __forceinline__ int64_t readlane64(int64_t v, int l) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-// Sum over the wave, returned as a wave-uniform (scalar) value.
-__device__ __forceinline__ int64_t wave_sum64(int64_t v) {
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) v += __shfl_xor(v, m, kWave);
-  return readlane64(v, 0);
+// One step of the wave scan below on a 64-bit value: the DPP move of both
+// halves (0 where the source lane is outside the row or the row is masked).
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ int64_t dpp_move64(int64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, kCtrl, kRowMask, 0xf, false);
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)((uint64_t)v >> 32), kCtrl, kRowMask, 0xf, false);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-__device__ __forceinline__ int64_t wave_incl_scan64(int64_t v, int lane) {
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int64_t u = __shfl_up(v, off, kWave);
-    if (lane >= off) v += u;
-  }
+// Inclusive prefix sum over the 64 lanes of a wave, in registers: four row
+// shifts give the sums within each 16-lane row, then the last lane of row 0
+// is added to row 1 and of row 2 to row 3, and lane 31 to rows 2 and 3.
+__device__ __forceinline__ int64_t wave_incl_scan64(int64_t v, int) {
+  v += dpp_move64<0x111, 0xf>(v);  // row_shr:1
+  v += dpp_move64<0x112, 0xf>(v);  // row_shr:2
+  v += dpp_move64<0x114, 0xf>(v);  // row_shr:4
+  v += dpp_move64<0x118, 0xf>(v);  // row_shr:8
+  v += dpp_move64<0x142, 0xa>(v);  // row_bcast:15 -> rows 1, 3
+  v += dpp_move64<0x143, 0xc>(v);  // row_bcast:31 -> rows 2, 3
   return v;
+}
+
+// Sum over the wave, returned as a wave-uniform (scalar) value.
+__device__ __forceinline__ int64_t wave_sum64(int64_t v) {
+  return readlane64(wave_incl_scan64(v, 0), kWave - 1);
 }
 
 // Balanced schedule (flash-decoding with split points balanced across rows).
