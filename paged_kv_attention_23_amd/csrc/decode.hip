@@ -655,6 +655,10 @@ void decode_balanced_kernel(DecodeArgs a) {
   if (threadIdx.x == 0) a.desc[(int64_t)g * W + w] = int4{desc_r, desc_slot, desc_last, 0};
 }
 
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
 // Merge of per-row split partials: one wave per (row, query head).
 //   M = max_s L_s; LSE = M + ln sum_s exp(L_s - M); O = sum_s exp(L_s - LSE) O_s
 // Partials with L_s = -inf carry weight zero and are not read.
@@ -677,35 +681,39 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(DecodeArgs a) {
 #pragma unroll
     for (int k = 0; k < kPer; ++k) pre[s][k] = (s < S) ? op[k] : 0.f;
   }
+  // Lane s < S holds split s's LSE; the max, the sum and the weights are
+  // wave-uniform, read lane by lane (S is at most 64) rather than through
+  // cross-lane shuffles.
   const float ls = (lane < S) ? a.lse_part[(int64_t)lane * nrh + rh] : -INFINITY;
-  float M = ls;
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) M = fmaxf(M, shfl_xor_f(M, m));
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, readlane_f(ls, s));
   if (M == -INFINITY) {
 #pragma unroll
     for (int k = 0; k < kPer; ++k) a.out[rh * D + lane * kPer + k] = 0;
     if (lane == 0) a.lse[rh] = -INFINITY;
     return;
   }
-  float w = (ls == -INFINITY) ? 0.f : expf(ls - M);
-  float sum = w;
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) sum += shfl_xor_f(sum, m);
+  float sum = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float Ls = readlane_f(ls, s);
+    if (Ls != -INFINITY) sum += expf(Ls - M);
+  }
   const float L = M + logf(sum);
-  w = (ls == -INFINITY) ? 0.f : expf(ls - L);
+  const float w = (ls == -INFINITY) ? 0.f : expf(ls - L);
   float acc[kPer];
 #pragma unroll
   for (int k = 0; k < kPer; ++k) acc[k] = 0.f;
 #pragma unroll
   for (int s = 0; s < kPre; ++s) {
-    const float ws = __shfl(w, s, kWave);
-    if (s >= S || ws == 0.f) continue;  // uniform: every lane sees the same ws
+    if (s >= S) break;
+    const float ws = readlane_f(w, s);
+    if (ws == 0.f) continue;  // uniform
 #pragma unroll
     for (int k = 0; k < kPer; ++k) acc[k] += ws * pre[s][k];
   }
   for (int s = kPre; s < S; ++s) {
-    const float ws = __shfl(w, s, kWave);
-    if (ws == 0.f) continue;  // uniform: every lane sees the same ws
+    const float ws = readlane_f(w, s);
+    if (ws == 0.f) continue;  // uniform
     const float *op = a.o_part + ((int64_t)s * nrh + rh) * D + lane * kPer;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) acc[k] += ws * op[k];
