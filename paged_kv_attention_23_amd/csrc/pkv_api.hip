@@ -483,6 +483,10 @@ static int prefill_common(const char *who, const void *q, const void *k, const v
   if ((int64_t)num_kv_heads * head_dim * 2 >= (1 << 24))  // one token's K row in bytes, a 24-bit product
     return fail(PKV_E_SHAPE, "%s: num_kv_heads*head_dim*2 must be below 2^24 (got %d heads)", who,
                 num_kv_heads);
+  // One workgroup per (query tile, KV head); a tile holds at least 8 rows.
+  if (((int64_t)total_len + 7) / 8 + num_docs > (int64_t)UINT32_MAX / num_kv_heads)
+    return fail(PKV_E_SHAPE, "%s: total_len %d with %d KV heads needs more than 2^32 workgroups",
+                who, total_len, num_kv_heads);
   if (fused) {
     int rc = check_pool(num_pages, page_size, num_kv_heads, head_dim, num_slots, max_blocks);
     if (rc) return rc;

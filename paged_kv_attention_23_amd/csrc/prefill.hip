@@ -507,6 +507,7 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
   const int QT = kPfRows / a.G;
   // Sum over documents of ceil(n_d / QT) is at most ceil(L / QT) + num_docs.
   const int64_t tiles = ((int64_t)a.L + QT - 1) / QT + a.num_docs;
+  if (tiles * a.H_kv > (int64_t)UINT32_MAX) return hipErrorInvalidConfiguration;  // grid would wrap
   const dim3 grid((unsigned)(tiles * a.H_kv));
   if (a.D == 64) {
     if (a.prefix_lens)

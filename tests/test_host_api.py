@@ -153,6 +153,9 @@ def test_prefill_checks(lib):
     # one token's K row (num_kv_heads*head_dim*2 bytes) must stay below 2^24
     assert f(FAKE, FAKE, FAKE, FAKE, 1, 10, 65536, 65536, 128, 0.1, FAKE, FAKE, 0) == -2
     assert "2^24" in B.last_error()
+    # a grid of more than 2^32 workgroups (tiles of 8 rows at 16 query heads per KV head)
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 2**31 - 1, 512, 32, 128, 0.1, FAKE, FAKE, 0) == -2
+    assert "2^32 workgroups" in B.last_error()
 
 
 def test_validate_checks(lib):
