@@ -137,8 +137,13 @@ __device__ bool find_tile(const int32_t *cu, int num_docs, int L, int QT, int qt
   return false;
 }
 
+// Waves per SIMD the register budget is sized for: at head_dim 64 the
+// kernel fits three (three workgroups per CU, 43 KB of LDS each).
+template <int D>
+constexpr int kPfWavesPerEu = D == 64 ? 3 : PKV_PF_WPE;
+
 template <int D, bool kFused, bool kPrefix>
-__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(PKV_PF_WPE)))
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(kPfWavesPerEu<D>)))
 void prefill_kernel(PrefillArgs a) {
   static_assert(kFused || !kPrefix, "a paged prefix comes with the chunk's scatter");
   using Gm = PfGeom<D>;
