@@ -475,13 +475,15 @@ void prefill_kernel(PrefillArgs a) {
       qk(h2, sc);
       softmax_pv(h2, sc);
     }
-    if (s + 1 < nsteps) {
+    if (s + 1 < nsteps) {  // uniform
       store_stage(buf ^ 1);
       if constexpr (kFused) {
         if (scatter) scatter_stage(s + 1);
       }
+      __syncthreads();  // stage s+1 is in LDS and every wave is done with stage s
     }
-    __syncthreads();
+    // After the last stage no wave touches the LDS again and each writes only
+    // its own rows, so the waves go on to the epilogue without a barrier.
   }
 
   // Normalise and write: lane holds O[row][d = 32*(t/2) + 8*lg + 4*(t%2) + i]
