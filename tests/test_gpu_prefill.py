@@ -84,6 +84,20 @@ def test_prefill_head_dim_64(spec):
     check_close(out, lse, out_ref, lse_ref, f"prefill D=64 seed{seed}")
 
 
+def test_prefill_many_documents():
+    """300 short documents, some empty: the tile search walks five 64-document chunks."""
+    print("prefill 300 documents", flush=True)
+    rng = np.random.default_rng(67)
+    lens = [int(x) for x in rng.integers(0, 41, 300)]
+    lens[::17] = [0] * len(lens[::17])
+    pc = make_prefill_case(name="many", seed=67, doc_lens=lens, H_q=32, H_kv=8, D=128,
+                           page_size=128, num_pages=sum(-(-n // 128) for n in lens) + 4,
+                           max_blocks=1)
+    out_ref, lse_ref = oracle.prefill_case(pc)
+    out, lse = _run(pc)
+    check_close(out, lse, out_ref, lse_ref, "prefill 300 documents")
+
+
 def test_prefill_growing_scores():
     """Key magnitudes grow along each document, with spikes late in it, so the running
     reference max of a query row moves again and again inside its tile: the path that
