@@ -363,12 +363,13 @@ def load_ceil():
     L.ceil_stream_units.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int,
                                     ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     L.ceil_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    L.ceil_prefill_shape.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int] * 4 + [ctypes.c_void_p] * 3
     P, I, U = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint32
     L.ceil_paged_units.argtypes = [P, P, ctypes.c_uint64, U, I, P, I, I, I, I, P, P, I, P, P]
     return L
 
 
-def ceilings(torch, timer, dev, db3, K):
+def ceilings(torch, timer, dev, db3, K, prefill=None):
     """What plain kernels of the attention kernels' shapes reach on this GPU."""
     L = load_ceil()
     out = {}
@@ -455,6 +456,25 @@ def ceilings(torch, timer, dev, db3, K):
                 "frac_of_hbm_peak": round(db3.kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "note": "decode_shape_stream with the paged lookups: batch_idx and kv_len, one "
                         "page-id window per unit, K/V rows through the page ids; no arithmetic"}
+        # the packed prefill's launch shape and memory traffic without its arithmetic
+        if prefill is not None and prefill["case"].D == 128:
+            pc, tz, NP = prefill["case"], prefill["tensors"], prefill["layers"]
+
+            def fpre(i):
+                j = i % NP
+                assert L.ceil_prefill_shape(tz["q"][j].data_ptr(), tz["k"][j].data_ptr(),
+                                            tz["v"][j].data_ptr(), tz["cu"].data_ptr(), pc.n_docs,
+                                            pc.L, pc.H_q, pc.H_kv, tz["out"].data_ptr(),
+                                            tz["lse"].data_ptr(), st()) == 0
+            ms = timer(fpre, K) / K
+            fl = pc.flops()
+            out["prefill_shape_stream"] = {
+                "us": round(ms * 1e3, 3), "flops_of_the_call": int(fl),
+                "tflops_if_at_this_time": round(fl / (ms * 1e-3) / 1e12, 1),
+                "frac_of_bf16_peak_if_at_this_time": round(fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                "note": "the packed prefill's grid and tile order, tile search, Q rows read once, "
+                        "each document's K/V streamed in 64-key stages (one in flight), output "
+                        "rows and LSEs written; no arithmetic. Cold: the same rotating input sets"}
         fsink = torch.zeros(1024, dtype=torch.float32, device=dev)
         iters, grid = 4000, 2 * cus
 
@@ -466,6 +486,26 @@ def ceilings(torch, timer, dev, db3, K):
                             "frac_of_peak": round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                             "kernel": "v_mfma_f32_16x16x32_bf16, 16 independent accumulators "
                                       "per wave, 2 waves per SIMD"}
+    # a plain device copy: reads and writes the same number of bytes (mixed traffic, as in
+    # prefill, whose compulsory bytes are 61% reads and 39% writes)
+    csrc = torch.ones(1024 ** 3 // 4, dtype=torch.float32, device=dev)  # past the Infinity Cache
+    cdst = torch.empty_like(csrc)
+    for _ in range(2):
+        cdst.copy_(csrc)
+    torch.cuda.synchronize()
+    e0, e1 = timer.events()
+    e0.record()
+    for _ in range(10):
+        cdst.copy_(csrc)
+    e1.record()
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    cb = 2 * csrc.numel() * 4
+    out["copy_read_write"] = {"gbs": round(cb / (ms * 1e-3) / 1e9, 1), "bytes_moved": cb,
+                              "frac_of_hbm_peak": round(cb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                              "note": "torch device copy of 1 GiB: bytes read plus bytes written "
+                                      "per second"}
+    del csrc, cdst
     n = 8192
     a = torch.randn((n, n), dtype=torch.bfloat16, device=dev)
     b = torch.randn((n, n), dtype=torch.bfloat16, device=dev)
@@ -577,6 +617,7 @@ def main():
                                            out=p_out, lse=p_lse)
 
         prefill = dict(case=pc, layers=NP, attn=prefill_attn,
+                       tensors=dict(q=p_q, k=p_k, v=p_v, cu=p_cu, out=p_out, lse=p_lse),
                        step=prefill_step_separate if args.separate else prefill_step_fused,
                        alt=prefill_step_fused if args.separate else prefill_step_separate)
 
@@ -819,7 +860,7 @@ def main():
         out["configs"] = cfgs
 
     if not args.no_ceilings:
-        out["ceilings"] = ceilings(torch, timer, dev, db, K)
+        out["ceilings"] = ceilings(torch, timer, dev, db, K, prefill)
         progress("ceilings measured")
 
     if args.cpu_seconds > 0:

@@ -50,8 +50,8 @@ constexpr int kQB = PKV_PF_QB;                       // 16-column blocks per wav
 constexpr int kPfRows = 16 * kQB * kPfWaves;         // (head, query) rows per workgroup
 constexpr int kPfBN = PKV_PF_BN;                     // keys per LDS stage (multiple of 32)
 constexpr int kHalves = kPfBN / 32;                  // 32-key steps per stage
-constexpr float kLazy = 8.f;                         // lazy-rescale threshold, log2 units
-constexpr float kLazyWeight = 256.f;                 // 2^kLazy: the largest weight a step keeps
+constexpr int kLazyLog2 = 8;                         // lazy-rescale threshold, log2 units
+constexpr float kLazyWeight = float(1 << kLazyLog2); // the largest weight a step keeps
 
 // Layout of one head_dim (64 or 128).  A K/V row of D bf16 values is D/8
 // 16-byte pieces; one pass of the workgroup's threads over a stage covers
@@ -429,7 +429,7 @@ void prefill_kernel(PrefillArgs a) {
           }
         }
         // Speculative weights against the current reference point m_run.  The
-        // reference must move only when some weight exceeds 2^kLazy; every
+        // reference must move only when some weight exceeds 2^kLazyLog2; every
         // weight is at most its lane's sum, so the sum the step needs anyway
         // is the test (it may fire on a step that could have stayed, never
         // miss one).  The rare step that moves it takes the column max (max

@@ -18,6 +18,13 @@
 //                      page ids of its first 64 blocks, then each 16-key
 //                      block's rows through its page id (no arithmetic on
 //                      the data either)
+//   ceil_prefill_shape the packed prefill's launch shape and memory traffic
+//                      with the arithmetic taken out: one workgroup per
+//                      (query tile of 128 (head, row) pairs, KV head) in the
+//                      same document-major order, finding its tile from
+//                      cu_seqlens, reading its Q rows once, streaming its
+//                      document's K/V rows in 64-key stages (one stage in
+//                      flight), and writing its output rows and LSEs
 //   ceil_mfma          back-to-back 16x16x32 bf16 matrix instructions,
 //                      16 independent accumulators per wave, two waves per
 //                      SIMD (the dense bf16 rate of the instruction the
@@ -153,6 +160,98 @@ __global__ __launch_bounds__(256) void paged_units_kernel(
   if (x == key) sink[u & 1023] = x;
 }
 
+// Inclusive prefix sum over the wave in registers (DPP row shifts, then the
+// row-15 and lane-31 broadcasts).
+__device__ __forceinline__ int scan64(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);
+  return x;
+}
+
+// Head dim 128, 128 (head, row) pairs per tile: QT = 128 / G rows.  Tiles
+// are numbered document by document, a document's last query tile first;
+// blockIdx = tile * H_kv + KV head.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void prefill_shape_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                          const uint16_t *__restrict__ v, const int32_t *__restrict__ cu,
+                          int num_docs, int L, int H_q, int H_kv, uint16_t *__restrict__ out,
+                          float *__restrict__ lse) {
+  constexpr int D = 128;
+  const int G = H_q / H_kv, QT = 128 / G;
+  const int g = blockIdx.x % H_kv, tile = blockIdx.x / H_kv;
+  const int lane = threadIdx.x & 63;
+  // tile -> (document, query tile)
+  int base = 0, doc = -1, qt = 0;
+  for (int d0 = 0; d0 < num_docs && doc < 0; d0 += 64) {
+    const int d = d0 + lane;
+    int t = 0;
+    if (d < num_docs) {
+      const int lo = min(max(cu[d], 0), L), hi = min(max(cu[d + 1], lo), L);
+      t = (hi - lo + QT - 1) / QT;
+    }
+    const int incl = scan64(t);
+    const uint64_t hit = __ballot(base + incl > tile);
+    if (hit) {
+      const int j = __builtin_ctzll(hit);
+      doc = d0 + j;
+      qt = base + __builtin_amdgcn_readlane(incl, j) - 1 - tile;
+    } else {
+      base += __builtin_amdgcn_readlane(incl, 63);
+    }
+  }
+  if (doc < 0) return;  // uniform
+  const int doc_start = min(max(cu[doc], 0), L), doc_end = min(max(cu[doc + 1], doc_start), L);
+  const int q_lo = doc_start + qt * QT, q_hi = min(doc_end, q_lo + QT);
+  const int k_end = q_hi - doc_start;  // keys of the tile's longest row
+  if (k_end <= 0) return;  // uniform; a found tile always has keys
+  const int col = threadIdx.x & 15, row0 = threadIdx.x >> 4;  // 16 lanes per 256-byte row
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  // Q: 128 rows of 256 bytes, row R = row0 + 16 i -> head R / QT, query q_lo + R % QT
+  int orow[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int R = row0 + 16 * i, hh = R / QT, qq = q_lo + R % QT;
+    orow[i] = (hh < G && qq < q_hi) ? qq * H_q + g * G + hh : -1;
+    if (orow[i] >= 0) acc ^= *reinterpret_cast<const u32x4 *>(q + (int64_t)orow[i] * D + col * 8);
+  }
+  // K/V: 64-key stages of the document's rows, one stage in flight
+  const int64_t rs = (int64_t)H_kv * D;  // elements between consecutive tokens
+  const uint16_t *kg = k + (int64_t)doc_start * rs + g * D + col * 8;
+  const uint16_t *vg = v + (int64_t)doc_start * rs + g * D + col * 8;
+  u32x4 ks[4], vs[4];
+  auto load = [&](int s0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = min(s0 + row0 + 16 * i, k_end - 1);
+      ks[i] = *reinterpret_cast<const u32x4 *>(kg + key * rs);
+      vs[i] = *reinterpret_cast<const u32x4 *>(vg + key * rs);
+    }
+  };
+  load(0);
+  for (int s0 = 0; s0 < k_end; s0 += 64) {
+    u32x4 k2[4], v2[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      k2[i] = ks[i];
+      v2[i] = vs[i];
+    }
+    if (s0 + 64 < k_end) load(s0 + 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc ^= k2[i] ^ v2[i];
+  }
+  // output rows and LSEs (values derived from everything read)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (orow[i] < 0) continue;
+    *reinterpret_cast<u32x4 *>(out + (int64_t)orow[i] * D + col * 8) = acc;
+    if (col == 0) lse[orow[i]] = __uint_as_float(acc.x);
+  }
+}
+
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void mfma_kernel(int iters, float key, float *sink) {
   const float s = (float)(threadIdx.x & 7) * 0.001f;
@@ -209,6 +308,23 @@ int ceil_paged_units(const void *kpool, const void *vpool, uint64_t plane_bytes,
                      (hipStream_t)stream, (const char *)kpool, (const char *)vpool, plane_bytes,
                      row_bytes, H_kv, page_table, max_blocks, page_shift, num_pages, num_slots,
                      batch_idx, kv_len, 0x9e3779b9u, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// Packed bf16 q [L][H_q][128], k/v [L][H_kv][128], cu_seqlens [num_docs+1];
+// writes out [L][H_q][128] and lse [L][H_q] (values meaningless).
+int ceil_prefill_shape(const void *q, const void *k, const void *v, const int32_t *cu_seqlens,
+                       int num_docs, int L, int H_q, int H_kv, void *out, float *lse,
+                       void *stream) {
+  if (!q || !k || !v || !cu_seqlens || !out || !lse || num_docs <= 0 || L <= 0 || H_kv <= 0 ||
+      H_q % H_kv != 0 || H_q / H_kv > 16 || 128 % (H_q / H_kv) != 0)
+    return -1;
+  const int64_t QT = 128 / (H_q / H_kv);
+  const int64_t grid = ((L + QT - 1) / QT + num_docs) * H_kv;
+  if (grid > 0x7fffffff) return -1;
+  hipLaunchKernelGGL(prefill_shape_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream,
+                     (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, cu_seqlens,
+                     num_docs, L, H_q, H_kv, (uint16_t *)out, lse);
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
