@@ -210,13 +210,16 @@ void prefill_shape_kernel(const uint16_t *__restrict__ q, const uint16_t *__rest
   if (k_end <= 0) return;  // uniform; a found tile always has keys
   const int col = threadIdx.x & 15, row0 = threadIdx.x >> 4;  // 16 lanes per 256-byte row
   u32x4 acc = {0u, 0u, 0u, 0u};
-  // Q: 128 rows of 256 bytes, row R = row0 + 16 i -> head R / QT, query q_lo + R % QT
+  // Q: 128 rows of 256 bytes, row R = row0 + 16 i -> head R / QT, query q_lo + R % QT;
+  // in flight together with the first K/V stage, as in the prefill
   int orow[8];
+  u32x4 qv[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int R = row0 + 16 * i, hh = R / QT, qq = q_lo + R % QT;
     orow[i] = (hh < G && qq < q_hi) ? qq * H_q + g * G + hh : -1;
-    if (orow[i] >= 0) acc ^= *reinterpret_cast<const u32x4 *>(q + (int64_t)orow[i] * D + col * 8);
+    qv[i] = u32x4{0u, 0u, 0u, 0u};
+    if (orow[i] >= 0) qv[i] = *reinterpret_cast<const u32x4 *>(q + (int64_t)orow[i] * D + col * 8);
   }
   // K/V: 64-key stages of the document's rows, one stage in flight
   const int64_t rs = (int64_t)H_kv * D;  // elements between consecutive tokens
@@ -232,6 +235,8 @@ void prefill_shape_kernel(const uint16_t *__restrict__ q, const uint16_t *__rest
     }
   };
   load(0);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc ^= qv[i];
   for (int s0 = 0; s0 < k_end; s0 += 64) {
     u32x4 k2[4], v2[4];
 #pragma unroll
