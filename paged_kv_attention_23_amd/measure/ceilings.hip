@@ -24,7 +24,8 @@
 //                      same document-major order, finding its tile from
 //                      cu_seqlens, reading its Q rows once, streaming its
 //                      document's K/V rows in 64-key stages (one stage in
-//                      flight), and writing its output rows and LSEs
+//                      flight), and writing its output rows and LSEs, at
+//                      the prefill's occupancy (its LDS footprint reserved)
 //   ceil_mfma          back-to-back 16x16x32 bf16 matrix instructions,
 //                      16 independent accumulators per wave, two waves per
 //                      SIMD (the dense bf16 rate of the instruction the
@@ -181,6 +182,12 @@ void prefill_shape_kernel(const uint16_t *__restrict__ q, const uint16_t *__rest
                           int num_docs, int L, int H_q, int H_kv, uint16_t *__restrict__ out,
                           float *__restrict__ lse) {
   constexpr int D = 128;
+  // The prefill kernel's LDS footprint (two 64-key K/V stages, 75,776 bytes),
+  // so that the probe runs at its occupancy: two workgroups per CU.
+  __shared__ uint32_t occ[75776 / 4];
+  occ[threadIdx.x] = blockIdx.x;
+  __syncthreads();
+  if (occ[(threadIdx.x + 1) & 255] == 0xdeadbeefu) lse[0] = 1.f;  // never true; keeps the array
   const int G = H_q / H_kv, QT = 128 / G;
   const int g = blockIdx.x % H_kv, tile = blockIdx.x / H_kv;
   const int lane = threadIdx.x & 63;
