@@ -260,7 +260,8 @@ int paged_decode_attn_append(const void *q, const void *k_new, const void *v_new
  *
  * total_len == 0 is a valid no-op.  Requirements: head_dim 64 or 128, num_q_heads a
  * multiple of num_kv_heads with at most 16 query heads per KV head, scale
- * finite and > 0.
+ * finite and > 0, and (total_len/8 + num_docs) * num_kv_heads below 2^32 (one
+ * workgroup per query tile and KV head).  A violation returns PKV_E_SHAPE.
  */
 int packed_prefill_attn(const void *q, const void *k, const void *v, const int32_t *cu_seqlens,
                         int32_t num_docs, int32_t total_len, int32_t num_q_heads,
