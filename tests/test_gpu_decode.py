@@ -284,6 +284,27 @@ def test_decode_balanced_plans(spec):
         assert torch.equal(out, o2) and torch.equal(lse, l2)
 
 
+def test_decode_max_splits_and_shares():
+    """The largest split count (PKV_MAX_SPLITS, most splits empty on the short rows) and
+    the largest balanced cut (one KV head and one 100k-key row: the plan's maximum of
+    two shares per CU), at 16 query heads per KV head."""
+    _print_case("decode max splits and shares")
+    lens = [100000, 65, 64, 63, 1, 0]
+    c = _small_case(81, 16, 1, 128, 64, lens, "shuffled")
+    out_ref, lse_ref = oracle.decode_case(c)
+    d = _Dev(c)
+    out, lse = d.decode(num_splits=pkv.PKV_MAX_SPLITS)
+    torch.cuda.synchronize()
+    check_close(out, lse, out_ref, lse_ref, "S=PKV_MAX_SPLITS")
+    assert np.all(host_bits(out)[5] == 0)
+    W = pkv.paged_decode_balanced_parts(c.B, c.H_kv, max(lens))
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert W == min(2 * cus, 4096)
+    out, lse = d.decode(num_splits=0, flags=pkv.PKV_F_BALANCED)
+    torch.cuda.synchronize()
+    check_close(out, lse, out_ref, lse_ref, f"balanced W={W}")
+    assert np.all(host_bits(out)[5] == 0)
+
 def test_decode_needles():
     """A dominating key at page edges and at n-1 is found; one at position n is ignored."""
     _print_case("decode needles")
