@@ -20,9 +20,10 @@
 //    layout is directly the B operand P^T of O^T = V^T P^T (the same scheme
 //    as the decode kernel); V^T operands come from gfx950's transposing LDS
 //    reads, which hand each lane one head_dim value at four keys.
-//  * K/V stages of 64 keys are double buffered in LDS (row stride padded by
-//    16 bytes against bank conflicts); the next stage's global loads are in
-//    flight while the current one is used.
+//  * K/V stages of 64 keys are double buffered in LDS and written by
+//    gfx950's global-to-LDS loads, so no registers stage them; rows are
+//    unpadded with their 16-byte chunks XOR-swizzled against bank conflicts.
+//    The next stage's loads are in flight while the current one is used.
 //  * Online softmax in base 2 in fp32; causal masking only on stages that
 //    reach the diagonal.  The weights are computed against the running
 //    reference max straight away; the column max is reduced across lanes
@@ -53,23 +54,31 @@ constexpr int kHalves = kPfBN / 32;                  // 32-key steps per stage
 constexpr int kLazyLog2 = 8;                         // lazy-rescale threshold, log2 units
 constexpr float kLazyWeight = float(1 << kLazyLog2); // the largest weight a step keeps
 
-// Layout of one head_dim (64 or 128).  A K/V row of D bf16 values is D/8
-// 16-byte pieces; one pass of the workgroup's threads over a stage covers
-// kRowsPerPass consecutive key rows (16 at D = 128, 32 at D = 64).  LDS rows
-// are padded (K by 16 bytes, V by 64) so that the 16 addresses of an operand
-// read group fall in distinct banks at either head_dim.
+// LDS layout of one head_dim (64 or 128).  A K or V row of D bf16 values is
+// 2*D bytes, unpadded, in kChunks chunks of 16 bytes; chunk c of row r is
+// stored at position c ^ swz(r).  The swizzle depends on r mod 16 only and
+// makes both operand reads conflict-free: the K reads of one instruction
+// take one chunk from each of 16 consecutive rows, which land on 16 distinct
+// positions (D = 128: swz is a bijection of r mod 16; D = 64: two rows share
+// 256 bytes of banks, and swz is a bijection over the 8 rows of each
+// parity), and the transposing V reads of 16 lanes take chunks 4q..4q+3 of 4
+// consecutive rows, which swz sends to disjoint groups of 4 positions (or to
+// the other half of the banks).
 template <int D>
 struct PfGeom {
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
-  static constexpr int kRowStride = 2 * D + 16;               // bytes per K row in LDS
-  static constexpr int kVRowStride = 2 * D + 64;              // bytes per V row in LDS
-  static constexpr int kKTileBytes = kPfBN * kRowStride;      // one K stage
-  static constexpr int kStageBytes = kKTileBytes + kPfBN * kVRowStride;  // K, then V
-  static constexpr int kSmem = 2 * kStageBytes;               // 2 stages
-  static constexpr int kPieces = D / 8;                       // 16-byte pieces per row
-  static constexpr int kRowsPerPass = kPfThreads / kPieces;   // rows per pass of the workgroup
-  static constexpr int kLoads = kPfBN / kRowsPerPass;         // passes per stage
-  static_assert(kRowsPerPass % 16 == 0 && kPfBN % kRowsPerPass == 0, "passes are 16-key aligned");
+  static constexpr int kRowBytes = 2 * D;                        // one K or V row
+  static constexpr int kChunks = kRowBytes / 16;                 // 16-byte chunks per row
+  static constexpr int kRowsPerLoad = 1024 / kRowBytes;          // rows one global-to-LDS load fills
+  static constexpr int kTileBytes = kPfBN * kRowBytes;           // K (or V) of one stage
+  static constexpr int kStageBytes = 2 * kTileBytes;             // K, then V
+  static constexpr int kLoadsPerWave = kPfBN / kRowsPerLoad / kPfWaves;  // per tensor and stage
+  static_assert(kLoadsPerWave * kRowsPerLoad * kPfWaves == kPfBN, "a stage is whole loads per wave");
+  static_assert(16 % kRowsPerLoad == 0, "a load's rows lie in one 16-key group");
+  static __device__ __forceinline__ int swz(int r) {
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  }
 };
 
 struct PfTile {
@@ -147,10 +156,8 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(kPfW
 void prefill_kernel(PrefillArgs a) {
   static_assert(kFused || !kPrefix, "a paged prefix comes with the chunk's scatter");
   using Gm = PfGeom<D>;
-  constexpr int kPfRowStride = Gm::kRowStride, kPfVRowStride = Gm::kVRowStride;
-  constexpr int kPfKTileBytes = Gm::kKTileBytes, kPfStageBytes = Gm::kStageBytes;
-  constexpr int kPieces = Gm::kPieces, kRowsPerPass = Gm::kRowsPerPass, kPfLoads = Gm::kLoads;
-  __shared__ __attribute__((aligned(16))) char smem[Gm::kSmem];
+  __shared__ __attribute__((aligned(1024))) char sA[Gm::kStageBytes];  // stage buffers
+  __shared__ __attribute__((aligned(1024))) char sB[Gm::kStageBytes];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int hl = lane & 15, lg = lane >> 4;
@@ -171,10 +178,8 @@ void prefill_kernel(PrefillArgs a) {
   // cached in the pages (paged prefix, chunked prefill), [prefix, k_end) are
   // this document's packed rows, position prefix + j at packed row
   // doc_start + j.  Without a paged prefix, prefix = 0.
-  // Fused scatter: the document's last query tile reads every packed key of
-  // the document (its key range ends at the document end), so it alone
-  // writes them into their pages, from the stage registers.  Skip rules as
-  // in paged_kv_append.
+  // Fused scatter: only the document's last query tile, whose key range ends
+  // at the document end, writes the document's packed keys into their pages.
   int slot = 0, prefix = 0;
   bool scatter = false;
   if constexpr (kFused) {
@@ -224,124 +229,115 @@ void prefill_kernel(PrefillArgs a) {
     }
   }
 
-  // Cooperative stage loads: piece p = threadIdx.x + 256*i -> key row p/(D/8), 16-byte column p%(D/8).
-  // Keys past k_end (last stage only) are clamped to the last key: they lie
-  // past every row's position, so their scores are masked and their
-  // probabilities are exactly 0 against finite values.
+  // K/V stages: kPfBN keys of K, then of V, in one of two LDS buffers (sA
+  // and sB are distinct arrays, so the compiler's wait counting can tell that
+  // loads into one buffer never alias reads of the other).  Stages are
+  // written by gfx950's global-to-LDS loads, so no register holds stage data:
+  // load j of a stage fills 1 KB, rows kRowsPerLoad*j .., lane l the row
+  // kRowsPerLoad*j + l/kChunks at position l%kChunks, which holds the row's
+  // global chunk (l%kChunks) ^ swz(row).  Keys past k_end (last stage only)
+  // are clamped to the last key: they lie past every row's position, so
+  // their scores are masked and their probabilities are exactly 0 against
+  // finite values.
   const int64_t row_stride = (int64_t)a.H_kv * D;  // elements between consecutive tokens
   const uint32_t row_bytes = (uint32_t)row_stride * 2u;  // < 2^24, checked on the host
-  const uint32_t col_bytes = (threadIdx.x % kPieces) * 16u;
-  const int row0 = threadIdx.x / kPieces;               // stage row of piece 0
-  const uint16_t *kg = a.k + (int64_t)g * D;
-  const uint16_t *vg = a.v + (int64_t)g * D;
+  const char *kg = reinterpret_cast<const char *>(a.k + (int64_t)g * D);
+  const char *vg = reinterpret_cast<const char *>(a.v + (int64_t)g * D);
   const int32_t *pt_row = kFused ? a.page_table + (int64_t)slot * a.max_blocks : nullptr;
+  const int page_mask = (1 << a.page_shift) - 1;
   // Cached prefix: page ids of the document's first 64 blocks, one per lane,
-  // loaded once.  In a stage inside the prefix, pass i covers the keys
-  // key0 + kRowsPerPass*i ..; each 16-key group of them lies in one page
-  // (pages hold >= 16 keys and the groups are 16-aligned), so each group
-  // needs one page id (a lane read) and one uniform base.
+  // loaded once.  A load instruction's rows lie in one 16-key group, so in a
+  // stage wholly inside the prefix each instruction needs one page id (a lane
+  // read) and every lane adds its row's offset in the page.
   int pwin = 0;
   if constexpr (kPrefix) {
-    const int nblk = (prefix + (1 << a.page_shift) - 1) >> a.page_shift;
+    const int nblk = (prefix + page_mask) >> a.page_shift;
     if (lane < nblk && lane < a.max_blocks) pwin = pt_row[lane];
   }
-  u32x4 stk[kPfLoads], stv[kPfLoads];
-  int spage[kPfLoads];  // fused scatter: page of each piece's key (0 = skip)
-  auto load_stage = [&](int s) {
-    const int key0 = s * kPfBN;  // position of the stage's first key
-    if (kPrefix && key0 + kPfBN <= prefix) {
-      // Whole stage in the cached prefix: one page per 16-key piece.
-      const int grow = kRowsPerPass == 16 ? row0 : (row0 & 15);  // the lane's row in its 16-key group
-      const uint32_t off = (uint32_t)grow * (uint32_t)(D * 2) + col_bytes;
+  // this KV head's planes of the pools, and a key's row in them (32-bit
+  // byte offsets: a plane is below 4 GiB, checked on the host)
+  const int64_t plane = (int64_t)g * a.plane_rows * D;
+  const char *kpool = reinterpret_cast<const char *>(kFused ? a.k_pool + plane : nullptr);
+  const char *vpool = reinterpret_cast<const char *>(kFused ? a.v_pool + plane : nullptr);
+  auto pool_off = [&](int page, int key) {
+    page = min(max(page, 0), a.num_pages - 1);
+    return (((uint32_t)page << a.page_shift) + (uint32_t)(key & page_mask)) * (2u * D);
+  };
+  const int lrow = lane / Gm::kChunks, lpos = lane % Gm::kChunks;
+  auto dma_stage = [&](int st, char *dst) {
+    const int key0 = st * kPfBN;
+    // sources first (a prefix stage may look its pages up), then the loads,
+    // so that no wait for a page id holds back loads already issued
+    const char *ks[Gm::kLoadsPerWave], *vs[Gm::kLoadsPerWave];
 #pragma unroll
-      for (int i = 0; i < kPfLoads; ++i) {
-        int key = key0 + kRowsPerPass * i;  // first key of the lane's 16-key group
-        int page;
-        if constexpr (kRowsPerPass == 16) {
-          const int blk = key >> a.page_shift;
-          page = blk < kWave ? __builtin_amdgcn_readlane(pwin, blk) : pt_row[blk];
-        } else {
-          page = 0;
-#pragma unroll
-          for (int j = 0; j < kRowsPerPass / 16; ++j) {  // one uniform page id per group
-            const int blk = (key + 16 * j) >> a.page_shift;
-            const int pj = blk < kWave ? __builtin_amdgcn_readlane(pwin, blk) : pt_row[blk];
-            if ((row0 >> 4) == j) page = pj;
-          }
-          key += 16 * (row0 >> 4);
-        }
-        page = min(max(page, 0), a.num_pages - 1);
-        const int64_t first = ((int64_t)g * a.plane_rows + ((int64_t)page << a.page_shift) +
-                               (key & ((1 << a.page_shift) - 1))) * D;
-        stk[i] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(a.k_pool + first) + off);
-        stv[i] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(a.v_pool + first) + off);
-      }
-    } else if (!kPrefix || key0 >= prefix) {
-      // This document's packed rows only: one uniform base per stage and
-      // 32-bit lane offsets.
-      const int64_t first = (int64_t)(tl.doc_start + key0 - prefix) * row_stride;
-      const char *kbs = reinterpret_cast<const char *>(kg + first);
-      const char *vbs = reinterpret_cast<const char *>(vg + first);
-      const int last = k_end - 1 - key0;  // last live row of the stage
-#pragma unroll
-      for (int i = 0; i < kPfLoads; ++i) {
-        const int r = min(row0 + kRowsPerPass * i, last);
-        const uint32_t off = __umul24((uint32_t)r, row_bytes) + col_bytes;
-        stk[i] = *reinterpret_cast<const u32x4 *>(kbs + off);
-        stv[i] = *reinterpret_cast<const u32x4 *>(vbs + off);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < kPfLoads; ++i) {
-        const int p = threadIdx.x + kPfThreads * i;
-        const int key = min(key0 + p / kPieces, k_end - 1);
-        if (key < prefix) {                 // cached prefix: through the page table
-          int page = pt_row[key >> a.page_shift];
-          page = min(max(page, 0), a.num_pages - 1);
-          const int64_t row = (int64_t)g * a.plane_rows + ((int64_t)page << a.page_shift) +
-                              (key & ((1 << a.page_shift) - 1));
-          stk[i] = *reinterpret_cast<const u32x4 *>(a.k_pool + row * D + (p % kPieces) * 8);
-          stv[i] = *reinterpret_cast<const u32x4 *>(a.v_pool + row * D + (p % kPieces) * 8);
-        } else {                            // this document's packed rows
-          const int64_t off = (int64_t)(tl.doc_start + key - prefix) * row_stride + (p % kPieces) * 8;
-          stk[i] = *reinterpret_cast<const u32x4 *>(kg + off);
-          stv[i] = *reinterpret_cast<const u32x4 *>(vg + off);
+    for (int i = 0; i < Gm::kLoadsPerWave; ++i) {
+      const int j = wave + kPfWaves * i;                  // load instruction of the stage
+      const int r = Gm::kRowsPerLoad * j + lrow;          // this lane's stage row
+      const uint32_t cb = (uint32_t)(lpos ^ Gm::swz(r)) << 4;  // its global chunk, in bytes
+      if (kPrefix && key0 + kPfBN <= prefix) {
+        // whole stage in the cached prefix: one page per load instruction
+        const int blk = (key0 + Gm::kRowsPerLoad * j) >> a.page_shift;  // uniform
+        const int page = blk < kWave ? __builtin_amdgcn_readlane(pwin, blk) : pt_row[blk];
+        const uint32_t off = pool_off(page, key0 + r) + cb;
+        ks[i] = kpool + off;
+        vs[i] = vpool + off;
+      } else if (!kPrefix || key0 >= prefix) {
+        // this document's packed rows only
+        const int64_t first = (int64_t)(tl.doc_start + key0 - prefix) * row_bytes;
+        const uint32_t off = __umul24((uint32_t)min(r, k_end - 1 - key0), row_bytes) + cb;
+        ks[i] = kg + first + off;
+        vs[i] = vg + first + off;
+      } else {
+        const int key = min(key0 + r, k_end - 1);
+        if (key < prefix) {  // cached prefix: through the page table
+          const uint32_t off = pool_off(pt_row[key >> a.page_shift], key) + cb;
+          ks[i] = kpool + off;
+          vs[i] = vpool + off;
+        } else {             // this document's packed rows
+          const int64_t off = (int64_t)(tl.doc_start + key - prefix) * row_bytes + cb;
+          ks[i] = kg + off;
+          vs[i] = vg + off;
         }
       }
     }
-    if constexpr (kFused) {
-      if (scatter) {
 #pragma unroll
-        for (int i = 0; i < kPfLoads; ++i) {
-          const int pos = key0 + row0 + kRowsPerPass * i;
-          const int blk = pos >> a.page_shift;
-          spage[i] = (pos >= prefix && pos < k_end && blk < a.max_blocks) ? pt_row[blk] : 0;
-        }
-      }
+    for (int i = 0; i < Gm::kLoadsPerWave; ++i) {
+      char *kd = dst + 1024 * (wave + kPfWaves * i), *vd = kd + Gm::kTileBytes;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(ks[i]),
+                                       (__attribute__((address_space(3))) void *)kd, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(vs[i]),
+                                       (__attribute__((address_space(3))) void *)vd, 16, 0, 0);
     }
   };
-  auto scatter_stage = [&](int s) {
+  // Fused scatter: the document's last query tile reads every packed key of
+  // the document (its key range ends at the document end), so it alone
+  // writes them into their pages, from the stage in LDS.  Skip rules as in
+  // paged_kv_append.  The page ids are looked up at the start of the stage.
+  constexpr int kScatterPer = kPfBN * Gm::kChunks / kPfThreads;  // chunks per thread and tensor
+  auto scatter_pages = [&](int st, int (&spage)[kScatterPer]) {
 #pragma unroll
-    for (int i = 0; i < kPfLoads; ++i) {
-      const int p = threadIdx.x + kPfThreads * i;
-      if (spage[i] > 0 && spage[i] < a.num_pages) {
-        const int pos = s * kPfBN + p / kPieces;
-        const int64_t row = (int64_t)g * a.plane_rows + ((int64_t)spage[i] << a.page_shift) +
-                            (pos & ((1 << a.page_shift) - 1));
-        // whole 256-byte rows, not read again here: past the caches
-        __builtin_nontemporal_store(stk[i], reinterpret_cast<u32x4 *>(a.k_pool + row * D + (p % kPieces) * 8));
-        __builtin_nontemporal_store(stv[i], reinterpret_cast<u32x4 *>(a.v_pool + row * D + (p % kPieces) * 8));
-      }
+    for (int i = 0; i < kScatterPer; ++i) {
+      const int pos = st * kPfBN + (threadIdx.x + kPfThreads * i) / Gm::kChunks;
+      const int blk = pos >> a.page_shift;
+      spage[i] = (pos >= prefix && pos < k_end && blk < a.max_blocks) ? pt_row[blk] : 0;
     }
   };
-  auto store_stage = [&](int buf) {
-    char *kb = smem + buf * kPfStageBytes;
-    char *vb = kb + kPfKTileBytes;
+  auto scatter_stage = [&](int st, const char *cur, const int (&spage)[kScatterPer]) {
 #pragma unroll
-    for (int i = 0; i < kPfLoads; ++i) {
+    for (int i = 0; i < kScatterPer; ++i) {
       const int p = threadIdx.x + kPfThreads * i;
-      *reinterpret_cast<u32x4 *>(kb + (p / kPieces) * kPfRowStride + (p % kPieces) * 16) = stk[i];
-      *reinterpret_cast<u32x4 *>(vb + (p / kPieces) * kPfVRowStride + (p % kPieces) * 16) = stv[i];
+      const int r = p / Gm::kChunks, c = p % Gm::kChunks;
+      const int pos = st * kPfBN + r;
+      const int page = spage[i];
+      if (page > 0 && page < a.num_pages) {
+        const uint32_t lo = (uint32_t)r * Gm::kRowBytes + ((uint32_t)(c ^ Gm::swz(r)) << 4);
+        const u32x4 kw = *reinterpret_cast<const u32x4 *>(cur + lo);
+        const u32x4 vw = *reinterpret_cast<const u32x4 *>(cur + Gm::kTileBytes + lo);
+        const int64_t row = (int64_t)g * a.plane_rows + ((int64_t)page << a.page_shift) + (pos & page_mask);
+        // whole rows, not read again here: past the caches
+        __builtin_nontemporal_store(kw, reinterpret_cast<u32x4 *>(a.k_pool + row * D + c * 8));
+        __builtin_nontemporal_store(vw, reinterpret_cast<u32x4 *>(a.v_pool + row * D + c * 8));
+      }
     }
   };
 
@@ -360,31 +356,30 @@ void prefill_kernel(PrefillArgs a) {
 
   const int nsteps = (k_end + kPfBN - 1) / kPfBN;
   const int q_first = prefix + (tl.q_lo - tl.doc_start);  // position of the tile's first row
-  load_stage(0);
-  store_stage(0);
-  if constexpr (kFused) {
-    if (scatter) scatter_stage(0);
-  }
-  __syncthreads();
-  for (int s = 0; s < nsteps; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < nsteps) load_stage(s + 1);
-    const char *kb = smem + buf * kPfStageBytes;
-    const char *vb = kb + kPfKTileBytes;
-    // Transposing V reads: within each 16-lane group, lane hl addresses key
-    // row 4*lg + hl/4 (plus the block's first key) at head_dim
-    // 32*(t/2) + 8*(hl%4) + 4*(t%2); the hardware hands lane hl the four
-    // keys' values at one head_dim.  (V rows are 320 bytes apart, so the 16
-    // addresses of a group fall in distinct banks.)
-    const char *v_tr = vb + (4 * lg + (hl >> 2)) * kPfVRowStride + 16 * (hl & 3);
+  // Operand reads.  K: lane (hl, lg) reads row 16*kb2 + hl (plus the half's
+  // first key), chunk lg + 4*ch.  V^T (transposing reads): within each
+  // 16-lane group, lane hl addresses key row 4*lg + hl/4 (plus the block's
+  // first key) at head_dim 32*(t/2) + 8*(hl%4) + 4*(t%2), i.e. chunk
+  // hl%4 + 4*(t/2), byte 8*(t%2) in it; the hardware hands lane hl the four
+  // keys' values at one head_dim.  A row's position swizzle depends on the
+  // row mod 16 alone, which is fixed per lane for both.
+  const int fk = Gm::swz(hl), fv = Gm::swz(4 * lg + (hl >> 2));
+  auto run_stage = [&](int s, const char *kb, char *nxt) {
+    int spage[kScatterPer];
+    if constexpr (kFused) {
+      if (scatter) scatter_pages(s, spage);
+    }
+    if (s + 1 < nsteps) dma_stage(s + 1, nxt);
+    const char *vb = kb + Gm::kTileBytes;
     // S^T blocks of a 32-key half: keys key0 + 16*kb2 + (4*lg + i), columns qb.
     auto qk = [&](int h2, f32x4 (&sc)[2][kQB]) {
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
         bf16x8 kop[D / 32];
-        const char *kr = kb + (32 * h2 + 16 * kb2 + hl) * kPfRowStride + 16 * lg;
+        const char *kr = kb + (32 * h2 + 16 * kb2 + hl) * Gm::kRowBytes;
 #pragma unroll
-        for (int ch = 0; ch < D / 32; ++ch) kop[ch] = as_bf16x8(*reinterpret_cast<const u32x4 *>(kr + 64 * ch));
+        for (int ch = 0; ch < D / 32; ++ch)
+          kop[ch] = as_bf16x8(*reinterpret_cast<const u32x4 *>(kr + (((lg + 4 * ch) ^ fk) << 4)));
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -398,17 +393,18 @@ void prefill_kernel(PrefillArgs a) {
       const int key0 = s * kPfBN + 32 * h2;  // position of the half's first key
       const bool diag = key0 + 31 >= q_first;  // some key may lie past some query row
       const bool first = key0 == 0;  // the tile's first step: m_run is still -inf, no speculation
-      // V^T operands from transposing LDS reads: lane (hl, lg) of step t
-      // gets head_dim d = 32*(t/2) + 8*(hl/4) + 4*(t%2) + hl%4 at keys
-      // kappa(lg, 0..3) and kappa(lg, 4..7), the key order of P^T.  All eight are read first, so
+      // V^T operands: lane (hl, lg) of step t gets head_dim
+      // d = 32*(t/2) + 8*(hl/4) + 4*(t%2) + hl%4 at keys kappa(lg, 0..3) and
+      // kappa(lg, 4..7), the key order of P^T.  All of them are read first, so
       // that a column block's PV products can be issued as soon as its
       // softmax is done and run on the matrix cores during the next block's.
+      const char *v_tr = vb + (32 * h2 + 4 * lg + (hl >> 2)) * Gm::kRowBytes;
       bf16x8 vop[D / 16];
 #pragma unroll
       for (int t = 0; t < D / 16; ++t) {
-        const int col = 64 * (t >> 1) + 8 * (t & 1);  // bytes: head_dim 32*(t/2) + 4*(t%2)
-        const u32x2 lo = lds_read_tr16(v_tr + (32 * h2) * kPfVRowStride + col);
-        const u32x2 hi = lds_read_tr16(v_tr + (32 * h2 + 16) * kPfVRowStride + col);
+        const int col = ((((hl & 3) + 4 * (t >> 1)) ^ fv) << 4) + 8 * (t & 1);
+        const u32x2 lo = lds_read_tr16(v_tr + col);
+        const u32x2 hi = lds_read_tr16(v_tr + 16 * Gm::kRowBytes + col);
         vop[t] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
       }
 #pragma unroll
@@ -475,15 +471,22 @@ void prefill_kernel(PrefillArgs a) {
       qk(h2, sc);
       softmax_pv(h2, sc);
     }
-    if (s + 1 < nsteps) {  // uniform
-      store_stage(buf ^ 1);
-      if constexpr (kFused) {
-        if (scatter) scatter_stage(s + 1);
-      }
-      __syncthreads();  // stage s+1 is in LDS and every wave is done with stage s
+    // The scatter of stage s comes last: the compiler's wait for its page ids
+    // also waits for stage s+1's loads, which the barrier waits for anyway.
+    if constexpr (kFused) {
+      if (scatter) scatter_stage(s, kb, spage);
     }
-    // After the last stage no wave touches the LDS again and each writes only
-    // its own rows, so the waves go on to the epilogue without a barrier.
+    // Stage s+1 has landed (the barrier's wait covers this wave's loads) and
+    // every wave is done with stage s.  After the last stage no wave touches
+    // the LDS again and each writes only its own rows, so the waves go on to
+    // the epilogue without a barrier.
+    if (s + 1 < nsteps) __syncthreads();
+  };
+  dma_stage(0, sA);
+  __syncthreads();
+  for (int s = 0; s < nsteps; s += 2) {  // two stages per pass: buffers fixed at each call
+    run_stage(s, sA, sB);
+    if (s + 1 < nsteps) run_stage(s + 1, sB, sA);
   }
 
   // Normalise and write: lane holds O[row][d = 32*(t/2) + 8*lg + 4*(t%2) + i]
