@@ -473,8 +473,8 @@ def ceilings(torch, timer, dev, db3, K, prefill=None):
                 "tflops_if_at_this_time": round(fl / (ms * 1e-3) / 1e12, 1),
                 "frac_of_bf16_peak_if_at_this_time": round(fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                 "note": "the packed prefill's grid and tile order, tile search, Q rows read once, "
-                        "each document's K/V streamed in 64-key stages (one in flight), output "
-                        "rows and LSEs written, at the prefill's occupancy (two workgroups per CU); "
+                        "each document's K/V streamed in 32-key stages (one in flight), output "
+                        "rows and LSEs written, at the prefill's occupancy (three workgroups per CU); "
                         "no arithmetic. Cold: the same rotating input sets"}
         fsink = torch.zeros(1024, dtype=torch.float32, device=dev)
         iters, grid = 4000, 2 * cus

@@ -39,18 +39,10 @@ namespace pkv {
 #ifndef PKV_PF_QB
 #define PKV_PF_QB 2
 #endif
-#ifndef PKV_PF_BN
-#define PKV_PF_BN 64
-#endif
-#ifndef PKV_PF_WPE
-#define PKV_PF_WPE 2
-#endif
 constexpr int kPfWaves = 4;
 constexpr int kPfThreads = kPfWaves * kWave;
 constexpr int kQB = PKV_PF_QB;                       // 16-column blocks per wave
 constexpr int kPfRows = 16 * kQB * kPfWaves;         // (head, query) rows per workgroup
-constexpr int kPfBN = PKV_PF_BN;                     // keys per LDS stage (multiple of 32)
-constexpr int kHalves = kPfBN / 32;                  // 32-key steps per stage
 constexpr int kLazyLog2 = 8;                         // lazy-rescale threshold, log2 units
 constexpr float kLazyWeight = float(1 << kLazyLog2); // the largest weight a step keeps
 
@@ -64,16 +56,16 @@ constexpr float kLazyWeight = float(1 << kLazyLog2); // the largest weight a ste
 // parity), and the transposing V reads of 16 lanes take chunks 4q..4q+3 of 4
 // consecutive rows, which swz sends to disjoint groups of 4 positions (or to
 // the other half of the banks).
-template <int D>
+template <int D, int BN>
 struct PfGeom {
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
   static constexpr int kRowBytes = 2 * D;                        // one K or V row
   static constexpr int kChunks = kRowBytes / 16;                 // 16-byte chunks per row
   static constexpr int kRowsPerLoad = 1024 / kRowBytes;          // rows one global-to-LDS load fills
-  static constexpr int kTileBytes = kPfBN * kRowBytes;           // K (or V) of one stage
+  static constexpr int kTileBytes = BN * kRowBytes;              // K (or V) of one stage
   static constexpr int kStageBytes = 2 * kTileBytes;             // K, then V
-  static constexpr int kLoadsPerWave = kPfBN / kRowsPerLoad / kPfWaves;  // per tensor and stage
-  static_assert(kLoadsPerWave * kRowsPerLoad * kPfWaves == kPfBN, "a stage is whole loads per wave");
+  static constexpr int kLoadsPerWave = BN / kRowsPerLoad / kPfWaves;  // per tensor and stage
+  static_assert(kLoadsPerWave * kRowsPerLoad * kPfWaves == BN, "a stage is whole loads per wave");
   static_assert(16 % kRowsPerLoad == 0, "a load's rows lie in one 16-key group");
   static __device__ __forceinline__ int swz(int r) {
     if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
@@ -146,16 +138,28 @@ __device__ bool find_tile(const int32_t *cu, int num_docs, int L, int QT, int qt
   return false;
 }
 
-// Waves per SIMD the register budget is sized for: at head_dim 64 the
-// kernel fits three (three workgroups per CU, 43 KB of LDS each).
-template <int D>
-constexpr int kPfWavesPerEu = D == 64 ? 3 : PKV_PF_WPE;
+// Per kernel: keys per LDS stage, waves per SIMD the registers are sized
+// for, and whether V^T operands are read right before their products
+// (fewer live registers) or all at once ahead of the softmax.  At head_dim
+// 128 the attention-only and chunked kernels run 32-key stages at three
+// waves per SIMD, three workgroups per CU (32 KB of LDS each); the fused
+// scatter kernel holds more registers and runs 64-key stages at two.  At
+// head_dim 64 every kernel fits three waves with 64-key stages.
+template <int D, bool kFused, bool kPrefix>
+struct PfTune {
+  static constexpr bool kWide = D == 64 || (kFused && !kPrefix);
+  static constexpr int kBN = kWide ? 64 : 32;
+  static constexpr int kWaves = (D == 128 && kFused && !kPrefix) ? 2 : 3;
+  static constexpr bool kJitV = kBN == 32;
+};
 
 template <int D, bool kFused, bool kPrefix>
-__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(kPfWavesPerEu<D>)))
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(PfTune<D, kFused, kPrefix>::kWaves)))
 void prefill_kernel(PrefillArgs a) {
   static_assert(kFused || !kPrefix, "a paged prefix comes with the chunk's scatter");
-  using Gm = PfGeom<D>;
+  using Tn = PfTune<D, kFused, kPrefix>;
+  constexpr int BN = Tn::kBN;  // keys per stage
+  using Gm = PfGeom<D, BN>;
   __shared__ __attribute__((aligned(1024))) char sA[Gm::kStageBytes];  // stage buffers
   __shared__ __attribute__((aligned(1024))) char sB[Gm::kStageBytes];
   const int lane = threadIdx.x & (kWave - 1);
@@ -229,7 +233,7 @@ void prefill_kernel(PrefillArgs a) {
     }
   }
 
-  // K/V stages: kPfBN keys of K, then of V, in one of two LDS buffers (sA
+  // K/V stages: BN keys of K, then of V, in one of two LDS buffers (sA
   // and sB are distinct arrays, so the compiler's wait counting can tell that
   // loads into one buffer never alias reads of the other).  Stages are
   // written by gfx950's global-to-LDS loads, so no register holds stage data:
@@ -265,7 +269,7 @@ void prefill_kernel(PrefillArgs a) {
   };
   const int lrow = lane / Gm::kChunks, lpos = lane % Gm::kChunks;
   auto dma_stage = [&](int st, char *dst) {
-    const int key0 = st * kPfBN;
+    const int key0 = st * BN;
     // sources first (a prefix stage may look its pages up), then the loads,
     // so that no wait for a page id holds back loads already issued
     const char *ks[Gm::kLoadsPerWave], *vs[Gm::kLoadsPerWave];
@@ -274,7 +278,7 @@ void prefill_kernel(PrefillArgs a) {
       const int j = wave + kPfWaves * i;                  // load instruction of the stage
       const int r = Gm::kRowsPerLoad * j + lrow;          // this lane's stage row
       const uint32_t cb = (uint32_t)(lpos ^ Gm::swz(r)) << 4;  // its global chunk, in bytes
-      if (kPrefix && key0 + kPfBN <= prefix) {
+      if (kPrefix && key0 + BN <= prefix) {
         // whole stage in the cached prefix: one page per load instruction
         const int blk = (key0 + Gm::kRowsPerLoad * j) >> a.page_shift;  // uniform
         const int page = blk < kWave ? __builtin_amdgcn_readlane(pwin, blk) : pt_row[blk];
@@ -313,11 +317,11 @@ void prefill_kernel(PrefillArgs a) {
   // the document (its key range ends at the document end), so it alone
   // writes them into their pages, from the stage in LDS.  Skip rules as in
   // paged_kv_append.  The page ids are looked up at the start of the stage.
-  constexpr int kScatterPer = kPfBN * Gm::kChunks / kPfThreads;  // chunks per thread and tensor
+  constexpr int kScatterPer = BN * Gm::kChunks / kPfThreads;  // chunks per thread and tensor
   auto scatter_pages = [&](int st, int (&spage)[kScatterPer]) {
 #pragma unroll
     for (int i = 0; i < kScatterPer; ++i) {
-      const int pos = st * kPfBN + (threadIdx.x + kPfThreads * i) / Gm::kChunks;
+      const int pos = st * BN + (threadIdx.x + kPfThreads * i) / Gm::kChunks;
       const int blk = pos >> a.page_shift;
       spage[i] = (pos >= prefix && pos < k_end && blk < a.max_blocks) ? pt_row[blk] : 0;
     }
@@ -327,7 +331,7 @@ void prefill_kernel(PrefillArgs a) {
     for (int i = 0; i < kScatterPer; ++i) {
       const int p = threadIdx.x + kPfThreads * i;
       const int r = p / Gm::kChunks, c = p % Gm::kChunks;
-      const int pos = st * kPfBN + r;
+      const int pos = st * BN + r;
       const int page = spage[i];
       if (page > 0 && page < a.num_pages) {
         const uint32_t lo = (uint32_t)r * Gm::kRowBytes + ((uint32_t)(c ^ Gm::swz(r)) << 4);
@@ -354,7 +358,7 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) o[qb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nsteps = (k_end + kPfBN - 1) / kPfBN;
+  const int nsteps = (k_end + BN - 1) / BN;
   const int q_first = prefix + (tl.q_lo - tl.doc_start);  // position of the tile's first row
   // Operand reads.  K: lane (hl, lg) reads row 16*kb2 + hl (plus the half's
   // first key), chunk lg + 4*ch.  V^T (transposing reads): within each
@@ -390,22 +394,26 @@ void prefill_kernel(PrefillArgs a) {
       }
     };
     auto softmax_pv = [&](int h2, const f32x4 (&sc)[2][kQB]) {
-      const int key0 = s * kPfBN + 32 * h2;  // position of the half's first key
+      const int key0 = s * BN + 32 * h2;  // position of the half's first key
       const bool diag = key0 + 31 >= q_first;  // some key may lie past some query row
       const bool first = key0 == 0;  // the tile's first step: m_run is still -inf, no speculation
       // V^T operands: lane (hl, lg) of step t gets head_dim
       // d = 32*(t/2) + 8*(hl/4) + 4*(t%2) + hl%4 at keys kappa(lg, 0..3) and
-      // kappa(lg, 4..7), the key order of P^T.  All of them are read first, so
+      // kappa(lg, 4..7), the key order of P^T.  Read either all first, so
       // that a column block's PV products can be issued as soon as its
-      // softmax is done and run on the matrix cores during the next block's.
+      // softmax is done and run on the matrix cores during the next block's,
+      // or each right before its products, after every block's softmax.
       const char *v_tr = vb + (32 * h2 + 4 * lg + (hl >> 2)) * Gm::kRowBytes;
-      bf16x8 vop[D / 16];
-#pragma unroll
-      for (int t = 0; t < D / 16; ++t) {
+      auto read_v = [&](int t) {
         const int col = ((((hl & 3) + 4 * (t >> 1)) ^ fv) << 4) + 8 * (t & 1);
         const u32x2 lo = lds_read_tr16(v_tr + col);
         const u32x2 hi = lds_read_tr16(v_tr + 16 * Gm::kRowBytes + col);
-        vop[t] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+        return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+      };
+      bf16x8 vop[Tn::kJitV ? 1 : D / 16], popq[kQB];
+      if constexpr (!Tn::kJitV) {
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) vop[t] = read_v(t);
       }
 #pragma unroll
       for (int qb = 0; qb < kQB; ++qb) {
@@ -459,14 +467,24 @@ void prefill_kernel(PrefillArgs a) {
         l_run[qb] += ps;
         const u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                           pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-        const bf16x8 pop = as_bf16x8(pw);
+        popq[qb] = as_bf16x8(pw);
+        if constexpr (!Tn::kJitV) {
 #pragma unroll
-        for (int t = 0; t < D / 16; ++t) o[qb][t] = mfma16x16x32(vop[t], pop, o[qb][t]);
+          for (int t = 0; t < D / 16; ++t) o[qb][t] = mfma16x16x32(vop[t], popq[qb], o[qb][t]);
+        }
+      }
+      if constexpr (Tn::kJitV) {
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) {
+          const bf16x8 v = read_v(t);
+#pragma unroll
+          for (int qb = 0; qb < kQB; ++qb) o[qb][t] = mfma16x16x32(v, popq[qb], o[qb][t]);
+        }
       }
     };
 #pragma unroll
-    for (int h2 = 0; h2 < kHalves; ++h2) {  // 32-key steps of the stage
-      if (s * kPfBN + 32 * h2 >= k_end) break;  // uniform
+    for (int h2 = 0; h2 < BN / 32; ++h2) {  // 32-key steps of the stage
+      if (s * BN + 32 * h2 >= k_end) break;  // uniform
       f32x4 sc[2][kQB];
       qk(h2, sc);
       softmax_pv(h2, sc);

@@ -23,9 +23,9 @@
 //                      (query tile of 128 (head, row) pairs, KV head) in the
 //                      same document-major order, finding its tile from
 //                      cu_seqlens, reading its Q rows once, streaming its
-//                      document's K/V rows in 64-key stages (one stage in
+//                      document's K/V rows in 32-key stages (one stage in
 //                      flight), and writing its output rows and LSEs, at
-//                      the prefill's occupancy (its LDS footprint reserved)
+//                      the prefill's occupancy (three workgroups per CU)
 //   ceil_mfma          back-to-back 16x16x32 bf16 matrix instructions,
 //                      16 independent accumulators per wave, two waves per
 //                      SIMD (the dense bf16 rate of the instruction the
@@ -176,15 +176,16 @@ __device__ __forceinline__ int scan64(int x) {
 // Head dim 128, 128 (head, row) pairs per tile: QT = 128 / G rows.  Tiles
 // are numbered document by document, a document's last query tile first;
 // blockIdx = tile * H_kv + KV head.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
 void prefill_shape_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                           const uint16_t *__restrict__ v, const int32_t *__restrict__ cu,
                           int num_docs, int L, int H_q, int H_kv, uint16_t *__restrict__ out,
                           float *__restrict__ lse) {
   constexpr int D = 128;
-  // The prefill kernel's LDS footprint (two 64-key K/V stages, 75,776 bytes),
-  // so that the probe runs at its occupancy: two workgroups per CU.
-  __shared__ uint32_t occ[75776 / 4];
+  // LDS reserved so that the probe runs at the attention kernel's occupancy,
+  // three workgroups per CU (its registers allow three): 48 KB admits three
+  // and not four.
+  __shared__ uint32_t occ[49152 / 4];
   occ[threadIdx.x] = blockIdx.x;
   __syncthreads();
   if (occ[(threadIdx.x + 1) & 255] == 0xdeadbeefu) lse[0] = 1.f;  // never true; keeps the array
@@ -228,14 +229,14 @@ void prefill_shape_kernel(const uint16_t *__restrict__ q, const uint16_t *__rest
     qv[i] = u32x4{0u, 0u, 0u, 0u};
     if (orow[i] >= 0) qv[i] = *reinterpret_cast<const u32x4 *>(q + (int64_t)orow[i] * D + col * 8);
   }
-  // K/V: 64-key stages of the document's rows, one stage in flight
+  // K/V: 32-key stages of the document's rows, one stage in flight
   const int64_t rs = (int64_t)H_kv * D;  // elements between consecutive tokens
   const uint16_t *kg = k + (int64_t)doc_start * rs + g * D + col * 8;
   const uint16_t *vg = v + (int64_t)doc_start * rs + g * D + col * 8;
-  u32x4 ks[4], vs[4];
+  u32x4 ks[2], vs[2];
   auto load = [&](int s0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
       const int key = min(s0 + row0 + 16 * i, k_end - 1);
       ks[i] = *reinterpret_cast<const u32x4 *>(kg + key * rs);
       vs[i] = *reinterpret_cast<const u32x4 *>(vg + key * rs);
@@ -244,16 +245,16 @@ void prefill_shape_kernel(const uint16_t *__restrict__ q, const uint16_t *__rest
   load(0);
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc ^= qv[i];
-  for (int s0 = 0; s0 < k_end; s0 += 64) {
-    u32x4 k2[4], v2[4];
+  for (int s0 = 0; s0 < k_end; s0 += 32) {
+    u32x4 k2[2], v2[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
       k2[i] = ks[i];
       v2[i] = vs[i];
     }
-    if (s0 + 64 < k_end) load(s0 + 64);
+    if (s0 + 32 < k_end) load(s0 + 32);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc ^= k2[i] ^ v2[i];
+    for (int i = 0; i < 2; ++i) acc ^= k2[i] ^ v2[i];
   }
   // output rows and LSEs (values derived from everything read)
 #pragma unroll
