@@ -138,26 +138,24 @@ __device__ bool find_tile(const int32_t *cu, int num_docs, int L, int QT, int qt
   return false;
 }
 
-// Per kernel: keys per LDS stage, waves per SIMD the registers are sized
+// Per head_dim: keys per LDS stage, waves per SIMD the registers are sized
 // for, and whether V^T operands are read right before their products
 // (fewer live registers) or all at once ahead of the softmax.  At head_dim
-// 128 the attention-only and chunked kernels run 32-key stages at three
-// waves per SIMD, three workgroups per CU (32 KB of LDS each); the fused
-// scatter kernel holds more registers and runs 64-key stages at two.  At
-// head_dim 64 every kernel fits three waves with 64-key stages.
-template <int D, bool kFused, bool kPrefix>
+// 128 every kernel runs 32-key stages at three waves per SIMD, three
+// workgroups per CU (32 KB of LDS each); at head_dim 64 64-key stages fit
+// three waves with all V^T operands read first.
+template <int D>
 struct PfTune {
-  static constexpr bool kWide = D == 64 || (kFused && !kPrefix);
-  static constexpr int kBN = kWide ? 64 : 32;
-  static constexpr int kWaves = (D == 128 && kFused && !kPrefix) ? 2 : 3;
+  static constexpr int kBN = D == 64 ? 64 : 32;
+  static constexpr int kWaves = 3;
   static constexpr bool kJitV = kBN == 32;
 };
 
 template <int D, bool kFused, bool kPrefix>
-__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(PfTune<D, kFused, kPrefix>::kWaves)))
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(PfTune<D>::kWaves)))
 void prefill_kernel(PrefillArgs a) {
   static_assert(kFused || !kPrefix, "a paged prefix comes with the chunk's scatter");
-  using Tn = PfTune<D, kFused, kPrefix>;
+  using Tn = PfTune<D>;
   constexpr int BN = Tn::kBN;  // keys per stage
   using Gm = PfGeom<D, BN>;
   __shared__ __attribute__((aligned(1024))) char sA[Gm::kStageBytes];  // stage buffers
@@ -182,13 +180,13 @@ void prefill_kernel(PrefillArgs a) {
   // cached in the pages (paged prefix, chunked prefill), [prefix, k_end) are
   // this document's packed rows, position prefix + j at packed row
   // doc_start + j.  Without a paged prefix, prefix = 0.
-  // Fused scatter: only the document's last query tile, whose key range ends
-  // at the document end, writes the document's packed keys into their pages.
+  // Fused scatter: each query tile writes its own rows' K/V into their pages,
+  // after its outputs.
   int slot = 0, prefix = 0;
-  bool scatter = false;
+  bool slot_ok = false;
   if constexpr (kFused) {
     slot = a.doc_slots[tl.doc];
-    const bool slot_ok = slot > 0 && slot < a.num_slots;
+    slot_ok = slot > 0 && slot < a.num_slots;
     if constexpr (kPrefix) {
       if (!slot_ok) {  // padding document: every row sees no key (+0, -inf)
 #pragma unroll
@@ -207,7 +205,6 @@ void prefill_kernel(PrefillArgs a) {
       }
       prefix = min(max(a.prefix_lens[tl.doc], 0), a.max_blocks << a.page_shift);
     }
-    scatter = tl.q_hi == tl.doc_end && slot_ok;
   }
   const int k_end = prefix + (tl.q_hi - tl.doc_start);
 
@@ -313,38 +310,6 @@ void prefill_kernel(PrefillArgs a) {
                                        (__attribute__((address_space(3))) void *)vd, 16, 0, 0);
     }
   };
-  // Fused scatter: the document's last query tile reads every packed key of
-  // the document (its key range ends at the document end), so it alone
-  // writes them into their pages, from the stage in LDS.  Skip rules as in
-  // paged_kv_append.  The page ids are looked up at the start of the stage.
-  constexpr int kScatterPer = BN * Gm::kChunks / kPfThreads;  // chunks per thread and tensor
-  auto scatter_pages = [&](int st, int (&spage)[kScatterPer]) {
-#pragma unroll
-    for (int i = 0; i < kScatterPer; ++i) {
-      const int pos = st * BN + (threadIdx.x + kPfThreads * i) / Gm::kChunks;
-      const int blk = pos >> a.page_shift;
-      spage[i] = (pos >= prefix && pos < k_end && blk < a.max_blocks) ? pt_row[blk] : 0;
-    }
-  };
-  auto scatter_stage = [&](int st, const char *cur, const int (&spage)[kScatterPer]) {
-#pragma unroll
-    for (int i = 0; i < kScatterPer; ++i) {
-      const int p = threadIdx.x + kPfThreads * i;
-      const int r = p / Gm::kChunks, c = p % Gm::kChunks;
-      const int pos = st * BN + r;
-      const int page = spage[i];
-      if (page > 0 && page < a.num_pages) {
-        const uint32_t lo = (uint32_t)r * Gm::kRowBytes + ((uint32_t)(c ^ Gm::swz(r)) << 4);
-        const u32x4 kw = *reinterpret_cast<const u32x4 *>(cur + lo);
-        const u32x4 vw = *reinterpret_cast<const u32x4 *>(cur + Gm::kTileBytes + lo);
-        const int64_t row = (int64_t)g * a.plane_rows + ((int64_t)page << a.page_shift) + (pos & page_mask);
-        // whole rows, not read again here: past the caches
-        __builtin_nontemporal_store(kw, reinterpret_cast<u32x4 *>(a.k_pool + row * D + c * 8));
-        __builtin_nontemporal_store(vw, reinterpret_cast<u32x4 *>(a.v_pool + row * D + c * 8));
-      }
-    }
-  };
-
   float m_run[kQB], l_run[kQB], neg_m[kQB];  // neg_m: -m_run, or 0 while m_run is -inf
   f32x4 o[kQB][D / 16];
 #pragma unroll
@@ -369,10 +334,6 @@ void prefill_kernel(PrefillArgs a) {
   // row mod 16 alone, which is fixed per lane for both.
   const int fk = Gm::swz(hl), fv = Gm::swz(4 * lg + (hl >> 2));
   auto run_stage = [&](int s, const char *kb, char *nxt) {
-    int spage[kScatterPer];
-    if constexpr (kFused) {
-      if (scatter) scatter_pages(s, spage);
-    }
     if (s + 1 < nsteps) dma_stage(s + 1, nxt);
     const char *vb = kb + Gm::kTileBytes;
     // S^T blocks of a 32-key half: keys key0 + 16*kb2 + (4*lg + i), columns qb.
@@ -489,11 +450,6 @@ void prefill_kernel(PrefillArgs a) {
       qk(h2, sc);
       softmax_pv(h2, sc);
     }
-    // The scatter of stage s comes last: the compiler's wait for its page ids
-    // also waits for stage s+1's loads, which the barrier waits for anyway.
-    if constexpr (kFused) {
-      if (scatter) scatter_stage(s, kb, spage);
-    }
     // Stage s+1 has landed (the barrier's wait covers this wave's loads) and
     // every wave is done with stage s.  After the last stage no wave touches
     // the LDS again and each writes only its own rows, so the waves go on to
@@ -527,6 +483,30 @@ void prefill_kernel(PrefillArgs a) {
       *reinterpret_cast<u32x4 *>(orow + 32 * c) = w;
     }
     if (lg == 0) a.lse[rh] = (l > 0.f) ? (m_run[qb] + log2f(l)) * kLn2 : -INFINITY;
+  }
+
+  // Fused scatter of this tile's own rows (positions prefix + q - doc_start),
+  // with paged_kv_append's skip rules.  The tile has just streamed these rows
+  // (its last keys), so they are read from L2; whole rows, not read again
+  // here, are stored past the caches.
+  if constexpr (kFused) {
+    if (slot_ok) {
+      const int n = (tl.q_hi - tl.q_lo) * Gm::kChunks;
+      for (int p = threadIdx.x; p < n; p += kPfThreads) {
+        const int q = tl.q_lo + p / Gm::kChunks, c = p % Gm::kChunks;
+        const int pos = prefix + (q - tl.doc_start);
+        const int blk = pos >> a.page_shift;
+        if (blk >= a.max_blocks) continue;
+        const int page = pt_row[blk];
+        if (page <= 0 || page >= a.num_pages) continue;
+        const int64_t src = ((int64_t)q * a.H_kv + g) * D + c * 8;
+        const u32x4 kw = *reinterpret_cast<const u32x4 *>(a.k + src);
+        const u32x4 vw = *reinterpret_cast<const u32x4 *>(a.v + src);
+        const int64_t row = (int64_t)g * a.plane_rows + ((int64_t)page << a.page_shift) + (pos & page_mask);
+        __builtin_nontemporal_store(kw, reinterpret_cast<u32x4 *>(a.k_pool + row * D + c * 8));
+        __builtin_nontemporal_store(vw, reinterpret_cast<u32x4 *>(a.v_pool + row * D + c * 8));
+      }
+    }
   }
 }
 
