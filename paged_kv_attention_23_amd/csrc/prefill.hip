@@ -142,12 +142,12 @@ __device__ bool find_tile(const int32_t *cu, int num_docs, int L, int QT, int qt
 // for, and whether V^T operands are read right before their products
 // (fewer live registers) or all at once ahead of the softmax.  At head_dim
 // 128 every kernel runs 32-key stages at three waves per SIMD, three
-// workgroups per CU (32 KB of LDS each); at head_dim 64 64-key stages fit
-// three waves with all V^T operands read first.
+// workgroups per CU (32 KB of LDS each); at head_dim 64, 64-key stages fit
+// four waves with all V^T operands read first.
 template <int D>
 struct PfTune {
   static constexpr int kBN = D == 64 ? 64 : 32;
-  static constexpr int kWaves = 3;
+  static constexpr int kWaves = D == 64 ? 4 : 3;
   static constexpr bool kJitV = kBN == 32;
 };
 
