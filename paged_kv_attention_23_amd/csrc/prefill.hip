@@ -20,10 +20,13 @@
 //    layout is directly the B operand P^T of O^T = V^T P^T (the same scheme
 //    as the decode kernel); V^T operands come from gfx950's transposing LDS
 //    reads, which hand each lane one head_dim value at four keys.
-//  * K/V stages of 64 keys are double buffered in LDS and written by
-//    gfx950's global-to-LDS loads, so no registers stage them; rows are
-//    unpadded with their 16-byte chunks XOR-swizzled against bank conflicts.
-//    The next stage's loads are in flight while the current one is used.
+//  * K/V stages (32 keys at head_dim 128, 64 at 64) are double buffered in
+//    LDS and written by gfx950's global-to-LDS loads, so no registers stage
+//    them; rows are unpadded with their 16-byte chunks XOR-swizzled against
+//    bank conflicts.  The next stage's loads are in flight while the current
+//    one is used.  The registers this frees let three workgroups share a CU
+//    (four at head_dim 64), which hides more of each tile's start-up and
+//    epilogue behind the other tiles' work.
 //  * Online softmax in base 2 in fp32; causal masking only on stages that
 //    reach the diagonal.  The weights are computed against the running
 //    reference max straight away; the column max is reduced across lanes
