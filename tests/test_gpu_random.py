@@ -98,3 +98,43 @@ def test_random_chunked_prefill(seed):
     torch.cuda.synchronize()
     check_close(out, lse, out_ref, lse_ref, f"random chunked seed{seed}")
     assert np.array_equal(host_bits(kd), kp) and np.array_equal(host_bits(vd), vp)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_packed_prefill(seed):
+    """Packed prefill, plain or with the fused scatter, over drawn document mixes (empty and
+    single-token documents included), GQA ratios, head dims and page sizes."""
+    from workloads import BF16_NAN, make_prefill_case
+    rng = np.random.default_rng(3000 + seed)
+    H_q, H_kv, ps, _, _, _ = _draw(rng)
+    n = int(rng.integers(1, 40))
+    lens = [int(x) for x in rng.integers(0, 600, n)]
+    for i in rng.choice(n, size=min(n, 3), replace=False):
+        lens[i] = int(rng.choice([0, 1, 2]))
+    D = int(rng.choice([64, 128]))
+    fused = bool(rng.random() < 0.5)
+    print(f"random packed prefill seed={seed} docs={n} G={H_q // H_kv} D={D} ps={ps} "
+          f"fused={fused}", flush=True)
+    pc = make_prefill_case(name="rand", seed=seed, doc_lens=lens, H_q=H_q, H_kv=H_kv, D=D,
+                           page_size=ps, num_pages=sum(-(-x // ps) for x in lens) + 2,
+                           max_blocks=max([-(-x // ps) for x in lens] + [1]))
+    if pc.L == 0:
+        pytest.skip("empty draw")
+    out_ref, lse_ref = oracle.prefill_case(pc)
+    q, k, v, cu = dev_bf16(pc.q), dev_bf16(pc.k), dev_bf16(pc.v), dev_i32(pc.cu_seqlens)
+    if not fused:
+        out, lse = pkv.packed_prefill_attn(q, k, v, cu, float(pc.scale))
+        torch.cuda.synchronize()
+        check_close(out, lse, out_ref, lse_ref, f"random packed seed{seed}")
+        return
+    shape = (pc.H_kv, pc.num_pages * ps, D)
+    kp0 = np.full(shape, BF16_NAN, np.uint16)
+    kd, vd = dev_bf16(kp0), dev_bf16(kp0)
+    slots = np.arange(1, pc.n_docs + 1, dtype=np.int32)
+    out, lse = pkv.packed_prefill_attn_append(q, k, v, cu, float(pc.scale), kd, vd,
+                                              dev_i32(pc.page_table), dev_i32(slots), ps)
+    torch.cuda.synchronize()
+    check_close(out, lse, out_ref, lse_ref, f"random fused prefill seed{seed}")
+    kr, vr = oracle.append_pages(kp0, kp0.copy(), pc.num_pages, ps, pc.page_table, pc.batch_idx,
+                                 pc.input_pos, pc.k, pc.v)
+    assert np.array_equal(host_bits(kd), kr) and np.array_equal(host_bits(vd), vr)
