@@ -285,3 +285,42 @@ def test_prefill_fused_scatter_edges(spec):
     kr, vr = oracle.append_pages(kp0, vp0, pc.num_pages, pc.page_size, pt, bidx, pc.input_pos,
                                  pc.k, pc.v)
     assert np.array_equal(kb, kr) and np.array_equal(vb, vr)
+
+
+def test_prefill_outputs_past_4gib():
+    """66 copies of one 8192-token document (L = 540,672): q and out span 4.4 GB each, so the
+    later documents' rows sit past every 32-bit byte offset from the array bases.  Sampled
+    rows of the first, a middle and the last copy match the oracle's decode of that row,
+    and every copy's outputs are bit-identical to the first's (a document's rows do not
+    depend on where it sits in the packing)."""
+    print("prefill past 4 GiB", flush=True)
+    n, copies = 8192, 66
+    base = make_prefill_case(name="big", seed=67, doc_lens=[n], H_q=32, H_kv=8, D=128,
+                             page_size=128, num_pages=n // 128 + 2, max_blocks=n // 128)
+    L = n * copies
+    assert L * base.H_q * base.D * 2 > 2**32
+    q = dev_bf16(base.q).repeat(copies, 1, 1)
+    k = dev_bf16(base.k).repeat(copies, 1, 1)
+    v = dev_bf16(base.v).repeat(copies, 1, 1)
+    cu = dev_i32(np.arange(copies + 1, dtype=np.int32) * n)
+    out, lse = pkv.packed_prefill_attn(q, k, v, cu, float(base.scale))
+    torch.cuda.synchronize()
+    del q, k, v
+    rng = np.random.default_rng(67)
+    pos = np.asarray(sorted(set([0, 1, 31, 32, 4095, 8191] + [int(x) for x in rng.integers(0, n, 6)])),
+                     dtype=np.int64)
+    kp0 = np.full((base.H_kv, base.num_pages * base.page_size, base.D), BF16_NAN, np.uint16)
+    kp, vp = oracle.append_pages(kp0, kp0.copy(), base.num_pages, base.page_size, base.page_table,
+                                 base.batch_idx, base.input_pos, base.k, base.v)
+    out_ref, lse_ref = oracle.decode(base.q[pos], kp, vp, base.num_pages, base.page_size,
+                                     base.page_table, base.batch_idx[pos],
+                                     np.zeros(len(pos), np.int32),
+                                     (base.input_pos[pos] + 1).astype(np.int32), base.scale)
+    for c in (0, copies // 2, copies - 1):
+        idx = torch.from_numpy(pos + c * n).cuda()
+        check_close(out.index_select(0, idx), lse.index_select(0, idx), out_ref, lse_ref,
+                    f"prefill copy {c} (sampled rows)")
+    first_o, first_l = out[:n].view(torch.int16), lse[:n]
+    for c in range(1, copies):
+        assert torch.equal(out[c * n:(c + 1) * n].view(torch.int16), first_o), c
+        assert torch.equal(lse[c * n:(c + 1) * n], first_l), c
