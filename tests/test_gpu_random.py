@@ -3,6 +3,8 @@ points against the float64 oracle: shapes, GQA ratios, page sizes, layouts, sche
 flags drawn together, so combinations the targeted tests do not name are covered too."""
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import pytest
 
@@ -18,6 +20,8 @@ if not torch.cuda.is_available():  # pragma: no cover
 import paged_kv_attention_23_amd as pkv  # noqa: E402
 from gpu_util import check_close, dev_bf16, dev_i32, host_bits  # noqa: E402
 
+# PKV_RANDOM_SWEEP=n multiplies the number of drawn cases per test (default 1).
+SWEEP = max(1, int(os.environ.get("PKV_RANDOM_SWEEP", "1")))
 GQA = [(8, 8), (16, 8), (32, 8), (12, 4), (16, 2), (16, 1), (32, 2)]
 
 
@@ -30,7 +34,7 @@ def _draw(rng):
     return H_q, H_kv, ps, B, lens, slots
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(12 * SWEEP))
 def test_random_decode(seed):
     rng = np.random.default_rng(1000 + seed)
     H_q, H_kv, ps, B, lens, slots = _draw(rng)
@@ -70,7 +74,7 @@ def test_random_decode(seed):
     assert np.array_equal(host_bits(kd), kp) and np.array_equal(host_bits(vd), vp)
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(8 * SWEEP))
 def test_random_chunked_prefill(seed):
     rng = np.random.default_rng(2000 + seed)
     H_q, H_kv, ps, B, _, slots = _draw(rng)
@@ -100,7 +104,7 @@ def test_random_chunked_prefill(seed):
     assert np.array_equal(host_bits(kd), kp) and np.array_equal(host_bits(vd), vp)
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(8 * SWEEP))
 def test_random_packed_prefill(seed):
     """Packed prefill, plain or with the fused scatter, over drawn document mixes (empty and
     single-token documents included), GQA ratios, head dims and page sizes."""
